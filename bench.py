@@ -1,0 +1,322 @@
+#!/usr/bin/env python3
+"""Throughput of the SubSpec substitute-draft hot path on one MI355X.
+
+Workload: the full 28-layer Qwen2.5-7B-shaped substitute stack (hidden 3584, MLP 18944,
+28/4 heads, head dim 128, vocab 152064), random-init int4 group-64 substitute weights
+quantized on the GPU from random-init bf16 weights, a 64-token chain-plus-branches draft
+tree of depth 48, KV context 2048. One measured step is one decode cycle of that
+workload: 48 draft expansion steps over the 64 tree slots (substitute stack + bf16 LM
+head + greedy top-6 child selection each), one bf16-weight target verify pass over the
+tree, row argmax of the seeded target logits and the greedy acceptance walk, with the
+accept length read back by the host.
+
+Printed: one JSON line. `value` is draft-tree tokens per second (48 * 64 tree tokens per
+cycle over the cycle time). The `roofline` object covers the dominant kernel, the fused
+int4 gate_up + SwiGLU GEMM, timed with HIP events on its own stream; `cpu_baseline` is the
+CPU oracle on a bounded sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+DRAFT_STEPS = 48
+TOPK = 6
+DRAFT_TEMP = 0.2
+L_STAR = 27
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--layers", type=int, default=None, help="override the layer count (debug only)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=20)
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ model construction
+
+def build_model(cfg, dev, n_layers):
+    import torch
+    import bit_quantized_draft_amd as bq
+    from synth import gen
+    from synth.configs import layer_shapes
+    torch.manual_seed(0)
+    draft_layers, target_layers = [], []
+    ones = torch.ones(cfg.H, dtype=torch.bfloat16, device=dev)
+    for li in range(n_layers):
+        d, t = {}, {}
+        for name, N, K in layer_shapes(cfg):
+            w = gen.torch_normal_bf16((N, K), cfg.w_std, 0, cfg.cid, gen.TID_W, li * 16 + gen.SLOT[name], dev)
+            d[name] = bq.quantize_substitute(w)
+            t[name] = w
+        kc = gen.torch_normal_bf16((cfg.nkv, cfg.C, cfg.hd), 1.0, 0, cfg.cid, gen.TID_KC, li, dev)
+        vc = gen.torch_normal_bf16((cfg.nkv, cfg.C, cfg.hd), 1.0, 0, cfg.cid, gen.TID_VC, li, dev)
+        for x in (d, t):
+            x.update(norm1=ones, norm2=ones, k_cache=kc, v_cache=vc)
+        draft_layers.append(d)
+        target_layers.append(t)
+        if li % 7 == 0:
+            log(f"  layer {li} built")
+    embed = gen.torch_normal_bf16((cfg.V, cfg.H), cfg.w_std, 0, cfg.cid, gen.TID_EMBED, 0, dev)
+    head = gen.torch_normal_bf16((cfg.V, cfg.H), cfg.w_std, 0, cfg.cid, gen.TID_LMHEAD, 0, dev)
+    kw = dict(V=cfg.V, embed=embed, final_norm=ones, lm_head=head, rope_theta=cfg.rope_theta,
+              rms_eps=cfg.eps)
+    draft = bq.SubstituteModel(cfg.H, cfg.I, cfg.nq, cfg.nkv, cfg.hd, draft_layers, **kw)
+    target = bq.SubstituteModel(cfg.H, cfg.I, cfg.nq, cfg.nkv, cfg.hd, target_layers, **kw)
+    torch.cuda.synchronize()
+    return draft, target
+
+
+def algorithmic_bytes_step(cfg, n_layers):
+    """Bytes one draft step must move: int4 weights + fp16 scale/zero, prefix KV once per
+    layer, activations at kernel boundaries, bf16 LM head and fp32 logits."""
+    from synth.configs import layer_shapes
+    T, C = cfg.T, cfg.C
+    w_params = sum(N * K for _, N, K in layer_shapes(cfg))
+    per_layer = 0.5625 * w_params
+    per_layer += 2 * cfg.nkv * C * cfg.hd * 2                        # prefix K and V, bf16
+    qkvN = (cfg.nq + 2 * cfg.nkv) * cfg.hd
+    per_layer += T * (cfg.H * 2 * 2 + qkvN * 2 * 2 + cfg.nq * cfg.hd * 2 * 2 + cfg.I * 2 * 2)
+    per_layer += 2 * cfg.nkv * T * cfg.hd * 2                        # tree K/V written
+    head = cfg.V * cfg.H * 2 + T * cfg.V * 4 + T * cfg.H * 2
+    return n_layers * per_layer + head
+
+
+# ------------------------------------------------------------------ CPU oracle baseline
+
+def cpu_baseline(cfg, n_layers):
+    import oracle
+    from synth import gen
+    from synth.configs import layer_shapes
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    T, C = cfg.T, cfg.C
+    log("cpu baseline: generating and quantizing one layer with the oracle (untimed)")
+    lw = {}
+    for name, N, K in layer_shapes(cfg):
+        w = gen.weight_bf16(N, K, cfg.w_std, seed=0, cid=cfg.cid, layer=0, slot=gen.SLOT[name])
+        lw[name] = oracle.quantize(w)
+    lw["norm1"] = gen.norm_gain_bf16(cfg.H)
+    lw["norm2"] = gen.norm_gain_bf16(cfg.H)
+    kc = gen.normal_bf16((cfg.nkv, C, cfg.hd), 1.0, 0, cfg.cid, gen.TID_KC, 0)
+    vc = gen.normal_bf16((cfg.nkv, C, cfg.hd), 1.0, 0, cfg.cid, gen.TID_VC, 0)
+    par = gen.tree_parents(T, cfg.tree, seed=0, cid=cfg.cid)
+    h = gen.normal_bf16((T, cfg.H), 1.0, 0, cfg.cid, gen.TID_HIDDEN)
+    head_rows = cfg.V // 16
+    head = gen.normal_bf16((head_rows, cfg.H), cfg.w_std, 0, cfg.cid, gen.TID_LMHEAD)
+    t0 = time.perf_counter()
+    oracle.layer64(oracle.bf16_to_f64(h), lw, kc, vc, par, C, cfg)
+    t_layer = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    x = oracle.rmsnorm64(oracle.bf16_to_f64(h), np.ones(cfg.H), cfg.eps)
+    oracle.matmul64(x, oracle.bf16_to_f64(head))
+    t_head = (time.perf_counter() - t0) * (cfg.V / head_rows)
+    t_step = n_layers * t_layer + t_head
+    return {"value": T / t_step, "unit": "draft-tree tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"one substitute layer (T={T}, C={C}, fp64, {t_layer:.2f} s) extrapolated "
+                       f"x{n_layers}, plus the LM head on 1/16 of its rows ({t_head:.2f} s after "
+                       f"scaling x16); one draft step, no verify pass")}
+
+
+# ------------------------------------------------------------------ profiling data
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.h", "kernels.h"):
+        with open(os.path.join(ROOT, "bit_quantized_draft_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(bytes_alg):
+    """HBM bytes per launch of the dominant kernel from committed PMC summaries, or None."""
+    path = os.path.join(ROOT, "profiles", "gate_up_swiglu_qwen7b_T64_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        d = json.load(fh)
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import bit_quantized_draft_amd as bq
+    from synth import gen
+    from synth.configs import get_config
+    cfg = get_config(3)
+    n_layers = args.layers or cfg.L
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    T, C, V = cfg.T, cfg.C, cfg.V
+    log(f"building {cfg.name}: {n_layers} layers, T={T}, C={C}")
+    draft, target = build_model(cfg, dev, n_layers)
+
+    par_np = gen.tree_parents(T, cfg.tree, cfg.depth_cap, seed=0, cid=cfg.cid)
+    tok_np = gen.tree_tokens(par_np, V, seed=0, cid=cfg.cid)
+    lg_np = gen.target_logits(par_np, tok_np, V, L_STAR, seed=0, cid=cfg.cid)
+    parents = torch.from_numpy(par_np).to(dev)
+    tokens = torch.from_numpy(tok_np).to(dev)
+    seeded_logits = torch.from_numpy(lg_np).to(dev)
+    mk = lambda: [torch.empty((cfg.nkv, T, cfg.hd), dtype=torch.bfloat16, device=dev) for _ in range(n_layers)]
+    tk_d, tv_d, tk_t, tv_t = mk(), mk(), mk(), mk()
+    logits = torch.empty((T, V), dtype=torch.float32, device=dev)
+    vlogits = torch.empty((T, V), dtype=torch.float32, device=dev)
+    children = torch.empty((T, TOPK), dtype=torch.int32, device=dev)
+    tgt = torch.empty(T, dtype=torch.int32, device=dev)
+    acc_out = (torch.empty(T, dtype=torch.int32, device=dev), torch.empty(1, dtype=torch.int32, device=dev),
+               torch.empty(1, dtype=torch.int32, device=dev))
+    inv_t = float(np.float32(1.0) / np.float32(DRAFT_TEMP))
+    ws_d = torch.empty(draft.workspace_bytes(T, C), dtype=torch.uint8, device=dev)
+    ws_t = torch.empty(target.workspace_bytes(T, C), dtype=torch.uint8, device=dev)
+
+    def draft_step():
+        draft.draft_tree_step(parents, C, tk_d, tv_d, tokens=tokens, logits=logits, workspace=ws_d)
+        bq.draft_select(logits, None, inv_t, TOPK, out=children)
+
+    def verify():
+        target.draft_tree_step(parents, C, tk_t, tv_t, tokens=tokens, logits=vlogits, workspace=ws_t)
+        bq.row_argmax(seeded_logits, out=tgt)
+        bq.tree_accept(parents, tokens, tgt, out=acc_out)
+
+    # eager reference results, then capture both phases in HIP graphs
+    draft_step(); verify()
+    torch.cuda.synchronize()
+    ref_children = children.clone()
+    ref_logits_row = logits[T - 1].clone()
+    ref_len = int(acc_out[1].item())
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g_draft, g_verify = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        draft_step(); verify()          # warm the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g_draft, stream=stream):
+            draft_step()
+        with torch.cuda.graph(g_verify, stream=stream):
+            verify()
+    torch.cuda.synchronize()
+    # every replay checked against the eager result, with eager work in between
+    for _ in range(2):
+        g_draft.replay(); g_verify.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(children, ref_children), "graph replay differs from eager run (children)"
+        assert torch.equal(logits[T - 1], ref_logits_row), "graph replay differs from eager run (logits)"
+        assert int(acc_out[1].item()) == ref_len
+        draft_step()
+        torch.cuda.synchronize()
+    assert ref_len == L_STAR, f"acceptance walk returned {ref_len}, expected {L_STAR}"
+
+    def cycle():
+        for _ in range(DRAFT_STEPS):
+            g_draft.replay()
+        g_verify.replay()
+        return int(acc_out[1].item())      # the one host read-back per cycle
+
+    log(f"warmup {args.warmup} cycles")
+    for _ in range(args.warmup):
+        cycle()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} cycles")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        L = cycle()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    assert L == L_STAR
+    ms_cycle = elapsed / args.steps * 1e3
+    value = DRAFT_STEPS * T * args.steps / elapsed
+
+    # phase split (outside the timed region): draft step alone and the verify phase alone
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(DRAFT_STEPS):
+        g_draft.replay()
+    e1.record(); torch.cuda.synchronize()
+    ms_draft_step = e0.elapsed_time(e1) / DRAFT_STEPS
+    e0.record(); g_verify.replay(); e1.record(); torch.cuda.synchronize()
+    ms_verify = e0.elapsed_time(e1)
+    step_bytes = algorithmic_bytes_step(cfg, n_layers)
+    step_gbs = step_bytes / (ms_draft_step * 1e-3) / 1e9
+
+    # dominant kernel: fused int4 gate_up + SwiGLU, 8 layers' weights in rotation (> 256 MB
+    # Infinity Cache), timed with HIP events recorded on the stream it runs on
+    x = gen.torch_normal_bf16((T, cfg.H), 1.0, 0, cfg.cid, gen.TID_X, 0, dev)
+    u = torch.empty((T, cfg.I), dtype=torch.bfloat16, device=dev)
+    rot = [draft.layers[i % n_layers]["gate_up"] for i in range(8)]
+    ks = torch.cuda.Stream()
+    with torch.cuda.stream(ks):
+        for q, s, z in rot:
+            bq.w4a16_gate_up_swiglu(x, q, s, z, out=u)
+        k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        k0.record(ks)
+        n_launch = 0
+        for _ in range(args.kernel_reps):
+            for q, s, z in rot:
+                bq.w4a16_gate_up_swiglu(x, q, s, z, out=u)
+                n_launch += 1
+        k1.record(ks)
+    torch.cuda.synchronize()
+    us_launch = k0.elapsed_time(k1) * 1e3 / n_launch
+    gu_bytes = 0.5625 * 2 * cfg.I * cfg.H + T * cfg.H * 2 + T * cfg.I * 2
+    achieved = gu_bytes / (us_launch * 1e-6) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, n_layers)
+
+    line = {
+        "metric": "draft-tree tokens/s per substitute-stack step; % of MI355X HBM roofline",
+        "value": round(value, 1), "unit": "draft-tree tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_cycle, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16+int4",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {n_layers}-layer substitute stack, T={T} tree tokens "
+                               f"(chain+branches, depth 48), C={C}, vocab {V}; cycle = {DRAFT_STEPS} "
+                               f"draft steps + bf16 verify pass + argmax + greedy accept",
+                   "tree_tokens_per_cycle": DRAFT_STEPS * T, "accept_len": L,
+                   "draft_step_ms": round(ms_draft_step, 4), "verify_ms": round(ms_verify, 4),
+                   "draft_step_alg_bytes": int(step_bytes),
+                   "draft_step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4)},
+        "roofline": {"kernel": "skinny_gemm_kernel<int4, EPI_SWIGLU> (gate_up 37888x3584, T=64)",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_from_profile(gu_bytes),
+                     "alg_bytes_per_launch": int(gu_bytes), "avg_launch_us": round(us_launch, 3)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,255 @@
+"""Python binding of the substitute-draft hot path: the C ABI names over torch tensors.
+
+Torch supplies device memory and the current stream; every step runs in the HIP
+library (libsubspec.so). Functions allocate their outputs with torch.empty when the
+caller passes none, check shapes/dtypes enough to marshal pointers, and raise
+SubspecError with the library's message on any error status.
+"""
+
+import ctypes
+
+import torch
+
+from ._lib import (SS_BF16, SS_W4G64, SsAttnArgs, SsLayer, SsLinear, SsModel, SsStepArgs,
+                   SubspecError, check, lib)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, dtype, name):
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous CUDA tensor of dtype {dtype}")
+
+
+def _workspace(nbytes, device, ws=None):
+    if nbytes == 0:
+        return None
+    if ws is not None and ws.numel() >= nbytes:
+        return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def abi_version():
+    return lib().ss_abi_version()
+
+
+# ------------------------------------------------------------------ substitute construction
+
+def quantize_substitute(w, group=64):
+    """bf16 W [n][k] -> (qweight u8 [n][k/2], scale fp16 [n][k/64], zero fp16 [n][k/64])."""
+    _need(w, torch.bfloat16, "w")
+    n, k = w.shape
+    q = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    s = torch.empty((n, k // 64), dtype=torch.float16, device=w.device)
+    z = torch.empty((n, k // 64), dtype=torch.float16, device=w.device)
+    check(lib().ss_quantize_substitute(_ptr(w), n, k, group, _ptr(q), _ptr(s), _ptr(z), _stream()))
+    return q, s, z
+
+
+def dequantize_substitute(q, s, z, group=64):
+    _need(q, torch.uint8, "qweight")
+    n, kh = q.shape
+    out = torch.empty((n, kh * 2), dtype=torch.float16, device=q.device)
+    check(lib().ss_dequantize_substitute(_ptr(q), _ptr(s), _ptr(z), n, kh * 2, group, _ptr(out),
+                                         _stream()))
+    return out
+
+
+# ------------------------------------------------------------------ linear layers
+
+def w4a16_linear(x, q, s, z, want_bf16=True, want_f32=True, workspace=None):
+    """Y = X deq(W)^T; returns (y_bf16 or None, y_f32 or None)."""
+    _need(x, torch.bfloat16, "x")
+    T, k = x.shape
+    n = q.shape[0]
+    yb = torch.empty((T, n), dtype=torch.bfloat16, device=x.device) if want_bf16 else None
+    yf = torch.empty((T, n), dtype=torch.float32, device=x.device) if want_f32 else None
+    nbytes = lib().ss_w4a16_linear_workspace(T, n, k)
+    ws = _workspace(nbytes, x.device, workspace)
+    check(lib().ss_w4a16_linear(_ptr(x), T, _ptr(q), _ptr(s), _ptr(z), n, k, _ptr(yb), _ptr(yf),
+                                _ptr(ws), nbytes, _stream()))
+    return yb, yf
+
+
+def w4a16_gate_up_swiglu(x, q, s, z, out=None, workspace=None):
+    """u = silu(X Wg^T) * (X Wu^T) with the fused int4 gate_up weight [2I][k]; u bf16 [T][I]."""
+    _need(x, torch.bfloat16, "x")
+    T, k = x.shape
+    I = q.shape[0] // 2
+    u = torch.empty((T, I), dtype=torch.bfloat16, device=x.device) if out is None else out
+    nbytes = lib().ss_w4a16_gate_up_swiglu_workspace(T, I, k)
+    ws = _workspace(nbytes, x.device, workspace)
+    check(lib().ss_w4a16_gate_up_swiglu(_ptr(x), T, _ptr(q), _ptr(s), _ptr(z), I, k, _ptr(u),
+                                        _ptr(ws), nbytes, _stream()))
+    return u
+
+
+def bf16_linear(x, w, want_bf16=True, want_f32=True, workspace=None):
+    _need(x, torch.bfloat16, "x")
+    _need(w, torch.bfloat16, "w")
+    T, k = x.shape
+    n = w.shape[0]
+    yb = torch.empty((T, n), dtype=torch.bfloat16, device=x.device) if want_bf16 else None
+    yf = torch.empty((T, n), dtype=torch.float32, device=x.device) if want_f32 else None
+    nbytes = lib().ss_bf16_linear_workspace(T, n, k)
+    ws = _workspace(nbytes, x.device, workspace)
+    check(lib().ss_bf16_linear(_ptr(x), T, _ptr(w), n, k, _ptr(yb), _ptr(yf), _ptr(ws), nbytes,
+                               _stream()))
+    return yb, yf
+
+
+# ------------------------------------------------------------------ tree
+
+def tree_validate(parents):
+    """CPU check of a parent array (list / numpy / CPU tensor). Returns True or raises."""
+    import numpy as np
+    p = np.ascontiguousarray(np.asarray(parents, dtype=np.int32))
+    check(lib().ss_tree_validate(p.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), len(p)))
+    return True
+
+
+def tree_mask(parents):
+    """Ancestor-or-self mask (int64 view of the uint64 words) [T][ceil(T/64)] and depth [T]."""
+    _need(parents, torch.int32, "parents")
+    T = parents.numel()
+    W = (T + 63) // 64
+    mask = torch.empty((T, W), dtype=torch.int64, device=parents.device)
+    depth = torch.empty(T, dtype=torch.int32, device=parents.device)
+    check(lib().ss_tree_mask(_ptr(parents), T, _ptr(mask), _ptr(depth), _stream()))
+    return mask, depth
+
+
+def tree_attention(q, k_cache, v_cache, k_tree, v_tree, parents, C, sm_scale=0.0,
+                   want_bf16=True, want_f32=False, want_mask=False, workspace=None):
+    """Tree attention; q [T][nq][hd], caches [nkv][c_stride][hd], tree K/V [nkv][T][hd]."""
+    _need(q, torch.bfloat16, "q")
+    T, nq, hd = q.shape
+    nkv, c_stride, _ = k_cache.shape
+    dev = q.device
+    out = torch.empty((T, nq, hd), dtype=torch.bfloat16, device=dev) if want_bf16 else None
+    outf = torch.empty((T, nq, hd), dtype=torch.float32, device=dev) if want_f32 else None
+    W = (T + 63) // 64
+    mask = torch.empty((T, W), dtype=torch.int64, device=dev) if want_mask else None
+    a = SsAttnArgs(q=q.data_ptr(), k_cache=k_cache.data_ptr(), v_cache=v_cache.data_ptr(),
+                   k_tree=k_tree.data_ptr(), v_tree=v_tree.data_ptr(), parents=parents.data_ptr(),
+                   out=None if out is None else out.data_ptr(),
+                   out_f32=None if outf is None else outf.data_ptr(),
+                   mask_out=None if mask is None else mask.data_ptr(),
+                   T=T, C=C, c_stride=c_stride, nq=nq, nkv=nkv, hd=hd, sm_scale=sm_scale)
+    nbytes = lib().ss_tree_attention_workspace(T, C, nq, nkv, hd)
+    ws = _workspace(nbytes, dev, workspace)
+    check(lib().ss_tree_attention(ctypes.byref(a), _ptr(ws), nbytes, _stream()))
+    return out, outf, mask
+
+
+# ------------------------------------------------------------------ verification / selection
+
+def row_argmax(logits, out=None):
+    _need(logits, torch.float32, "logits")
+    R, V = logits.shape
+    out = torch.empty(R, dtype=torch.int32, device=logits.device) if out is None else out
+    check(lib().ss_row_argmax(_ptr(logits), R, V, _ptr(out), _stream()))
+    return out
+
+
+def tree_accept(parents, tokens, target_argmax, out=None):
+    """Returns device tensors (path [T], accept_len [1], bonus [1])."""
+    T = parents.numel()
+    dev = parents.device
+    if out is None:
+        path = torch.empty(T, dtype=torch.int32, device=dev)
+        ln = torch.empty(1, dtype=torch.int32, device=dev)
+        bonus = torch.empty(1, dtype=torch.int32, device=dev)
+    else:
+        path, ln, bonus = out
+    check(lib().ss_tree_accept(_ptr(parents), _ptr(tokens), _ptr(target_argmax), T, _ptr(path),
+                               _ptr(ln), _ptr(bonus), _stream()))
+    return path, ln, bonus
+
+
+def draft_select(logits, gumbel, inv_temp, k, out=None):
+    _need(logits, torch.float32, "logits")
+    R, V = logits.shape
+    out = torch.empty((R, k), dtype=torch.int32, device=logits.device) if out is None else out
+    check(lib().ss_draft_select(_ptr(logits), _ptr(gumbel), R, V, float(inv_temp), k, _ptr(out),
+                                _stream()))
+    return out
+
+
+# ------------------------------------------------------------------ the draft step
+
+def linear_desc(entry):
+    """(qweight, scale, zero) tuple -> int4 descriptor; a bf16 tensor -> dense descriptor."""
+    if isinstance(entry, tuple):
+        q, s, z = entry
+        return SsLinear(kind=SS_W4G64, qweight=q.data_ptr(), scale=s.data_ptr(), zero=z.data_ptr(),
+                        w=None)
+    return SsLinear(kind=SS_BF16, qweight=None, scale=None, zero=None, w=entry.data_ptr())
+
+
+class SubstituteModel:
+    """Borrowed descriptor of a stack: per-layer weights (int4 tuples or bf16), norms, KV caches.
+
+    layers: list of dicts with keys qkv, o, gate_up, down, norm1, norm2, k_cache, v_cache.
+    The tensors stay owned by the caller (this object only keeps references).
+    """
+
+    def __init__(self, H, I, nq, nkv, hd, layers, V=0, embed=None, final_norm=None,
+                 lm_head=None, rope_theta=1e6, rms_eps=1e-6):
+        self.layers = layers
+        self.keep = (embed, final_norm, lm_head)
+        L = len(layers)
+        c_stride = layers[0]["k_cache"].shape[1]
+        self._layer_arr = (SsLayer * L)()
+        for i, ly in enumerate(layers):
+            self._layer_arr[i] = SsLayer(
+                norm1=ly["norm1"].data_ptr(), norm2=ly["norm2"].data_ptr(),
+                qkv=linear_desc(ly["qkv"]), o=linear_desc(ly["o"]),
+                gate_up=linear_desc(ly["gate_up"]), down=linear_desc(ly["down"]),
+                k_cache=ly["k_cache"].data_ptr(), v_cache=ly["v_cache"].data_ptr())
+        self.desc = SsModel(H=H, I=I, nq=nq, nkv=nkv, hd=hd, L=L, V=V, rope_theta=rope_theta,
+                            rms_eps=rms_eps, c_stride=c_stride,
+                            embed=None if embed is None else embed.data_ptr(),
+                            final_norm=None if final_norm is None else final_norm.data_ptr(),
+                            lm_head=None if lm_head is None else lm_head.data_ptr(),
+                            layers=self._layer_arr)
+        self.H, self.I, self.nq, self.nkv, self.hd, self.L, self.V = H, I, nq, nkv, hd, L, V
+        self._ws = None
+
+    def workspace_bytes(self, T, C):
+        return lib().ss_draft_tree_step_workspace(ctypes.byref(self.desc), T, C)
+
+    def draft_tree_step(self, parents, C, tree_k, tree_v, tokens=None, hidden_in=None,
+                        hidden_out=None, logits=None, logit_rows=None, workspace=None):
+        """One substitute-stack step over the T tree tokens (outputs written in place)."""
+        T = parents.numel()
+        L = self.L
+        tk = (ctypes.c_void_p * L)(*[t.data_ptr() for t in tree_k])
+        tv = (ctypes.c_void_p * L)(*[t.data_ptr() for t in tree_v])
+        a = SsStepArgs(tokens=None if tokens is None else tokens.data_ptr(),
+                       parents=parents.data_ptr(), T=T, C=C, tree_k=tk, tree_v=tv,
+                       hidden_in=None if hidden_in is None else hidden_in.data_ptr(),
+                       hidden_out=None if hidden_out is None else hidden_out.data_ptr(),
+                       logits=None if logits is None else logits.data_ptr(),
+                       logit_rows=None if logit_rows is None else logit_rows.data_ptr(),
+                       n_logit_rows=0 if logit_rows is None else logit_rows.numel())
+        nbytes = self.workspace_bytes(T, C)
+        if workspace is None:
+            if self._ws is None or self._ws.numel() < nbytes:
+                self._ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=parents.device)
+            workspace = self._ws
+        check(lib().ss_draft_tree_step(ctypes.byref(self.desc), ctypes.byref(a),
+                                       ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                       _stream()))
+
+
+__all__ = ["abi_version", "quantize_substitute", "dequantize_substitute", "w4a16_linear",
+           "w4a16_gate_up_swiglu",
+           "bf16_linear", "tree_validate", "tree_mask", "tree_attention", "row_argmax",
+           "tree_accept", "draft_select", "SubstituteModel", "SubspecError"]

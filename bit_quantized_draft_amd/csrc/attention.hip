@@ -1,0 +1,330 @@
+// Tree mask and tree-masked grouped-query attention over the KV cache shared with the target.
+//
+// The draft reads the target's KV cache for the committed prefix, so draft and target
+// attend over the same context (Review page "SubSpec: Using the Target Model's Own
+// Low-Bit Shadow as Its Draft Model", §4.1; Summary page "Speculate Deep and Accurate
+// ...", "Approach"). Each tree node additionally sees the tree keys of its own root
+// path (Review §6.3, token-tree verification).
+//
+// Key sequence of query token t: prefix keys 0..C-1 (always visible), then tree keys
+// C..C+T-1, tree key C+j visible iff bit j of t's ancestor-or-self mask is set.
+//
+// Layout on gfx950: all query rows of one KV head (grp = nq/nkv heads x T tokens) are
+// packed as the columns of one MFMA operand, so each K/V tile is read once per KV
+// head. Scores are computed transposed, S^T = K Q^T (v_mfma_f32_16x16x32_bf16 with
+// keys as rows), which leaves every lane holding one query row's scores for 8 keys:
+// exactly the B operand that O^T = V^T P^T needs, so P never leaves registers. V is
+// staged transposed in LDS. The online softmax runs in fp32 per query row (exp2 with
+// the scale folded in); the key sequence is split across workgroups and a second
+// kernel merges the partial (max, sum, O) triples in fixed order.
+#include "common.h"
+#include "kernels.h"
+
+namespace ss {
+
+// ------------------------------------------------------------------ tree mask
+
+// One thread per node walks its parent chain (at most T steps). Invalid parents stop
+// the walk and raise the error word, so an invalid tree never reads out of bounds.
+// T <= 256, so a row has at most 4 mask words.
+__global__ __launch_bounds__(256) void tree_mask_kernel(const int32_t* __restrict__ parents, int T,
+                                                        uint64_t* __restrict__ mask,
+                                                        int32_t* __restrict__ depth,
+                                                        int32_t* __restrict__ err) {
+  const int W = (T + 63) >> 6;
+  // this kernel opens every call that uses the error word: clear it first (no memset
+  // node, so the call sequence can be captured in a graph)
+  if (err) {
+    if (threadIdx.x == 0) *err = 0;
+    __syncthreads();
+  }
+  for (int i = threadIdx.x; i < T; i += blockDim.x) {
+    uint64_t words[4] = {0, 0, 0, 0};
+    int cur = i, d = 0, steps = 0;
+    bool bad = (i == 0) ? (parents[0] != -1) : false;
+    while (true) {
+      words[cur >> 6] |= 1ull << (cur & 63);
+      if (cur == 0) break;
+      const int p = parents[cur];
+      if (p < 0 || p >= cur || ++steps > T) { bad = true; break; }
+      cur = p;
+      ++d;
+    }
+    for (int w = 0; w < W; ++w) mask[(size_t)i * W + w] = words[w];
+    if (depth) depth[i] = d;
+    if (bad && err) atomicOr(err, 1);
+  }
+}
+
+hipError_t launch_tree_mask(const int32_t* parents, int T, uint64_t* mask, int32_t* depth,
+                            int32_t* err, hipStream_t st) {
+  hipLaunchKernelGGL(tree_mask_kernel, dim3(1), dim3(256), 0, st, parents, T, mask, depth, err);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ attention
+
+constexpr int KT = 32;                 // keys per tile
+constexpr int VT_STRIDE = KT + 4;      // halfs per transposed-V row (72 B, 8-B aligned)
+
+struct AttnParams {
+  const uint16_t* q;
+  const uint16_t* kc;
+  const uint16_t* vc;
+  const uint16_t* kt;
+  const uint16_t* vt;
+  const uint64_t* mask;
+  int T, C, c_stride, nq, nkv, grp, rows;  // rows = grp * T query rows per KV head
+  int keys_per_split, splits;
+  float scale_log2;                        // sm_scale * log2(e)
+  float* o_part;                           // [splits][nkv][rows][HD]
+  float* ml_part;                          // [splits][nkv][rows][2]  (max in log2 units, sum)
+};
+
+template <int HD, int QC>
+__global__ __launch_bounds__(256) void tree_attn_kernel(AttnParams p) {
+  constexpr int NW = 4;
+  constexpr int HC = HD / 32;               // 32-wide hd chunks
+  constexpr int DT = HD / 16;               // 16-wide d tiles of the output
+  constexpr int K_STRIDE = HD + 8;          // halfs per K row in LDS (pad against bank conflicts)
+  __shared__ __align__(16) uint16_t k_lds[KT * K_STRIDE];
+  __shared__ __align__(16) uint16_t vt_lds[HD * VT_STRIDE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j = lane & 15, b = lane >> 4;
+  const int kv = blockIdx.y;
+  const int split = blockIdx.z;
+  const int row_block = blockIdx.x * NW * QC * 16 + wave * QC * 16;
+  const int W = (p.T + 63) >> 6;
+  const int key_begin = split * p.keys_per_split;
+  const int key_end = min(p.C + p.T, key_begin + p.keys_per_split);
+
+  // Q fragments (B operand of S^T = K Q^T): lane (j, b) holds Q[row j][hd 8b..8b+7] per chunk
+  bf16x8_t qf[QC][HC];
+  int qtok[QC];
+  bool qvalid[QC];
+#pragma unroll
+  for (int c = 0; c < QC; ++c) {
+    const int r = row_block + c * 16 + j;
+    qvalid[c] = r < p.rows;
+    const int t = qvalid[c] ? r / p.grp : 0;
+    const int h = kv * p.grp + (qvalid[c] ? r % p.grp : 0);
+    qtok[c] = t;
+#pragma unroll
+    for (int hc = 0; hc < HC; ++hc) {
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (qvalid[c]) v = *reinterpret_cast<const u32x4_t*>(p.q + ((size_t)t * p.nq + h) * HD + hc * 32 + b * 8);
+      qf[c][hc] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+
+  f32x4_t o[QC][DT];
+  float m_run[QC], l_run[QC];
+#pragma unroll
+  for (int c = 0; c < QC; ++c) {
+    m_run[c] = -INFINITY;
+    l_run[c] = 0.f;
+#pragma unroll
+    for (int d = 0; d < DT; ++d) o[c][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  for (int k0 = key_begin; k0 < key_end; k0 += KT) {
+    // ---- stage K tile [KT][HD] and V^T tile [HD][KT]
+    constexpr int CHUNKS = KT * HD / 8;     // 16-byte chunks per tile
+    for (int ci = tid; ci < CHUNKS; ci += NW * 64) {
+      const int key = ci / (HD / 8), d0 = (ci % (HD / 8)) * 8;
+      const int kk = k0 + key;
+      u32x4_t kvv = {0u, 0u, 0u, 0u}, vvv = {0u, 0u, 0u, 0u};
+      if (kk < key_end) {
+        const uint16_t *ks, *vs;
+        if (kk < p.C) {
+          ks = p.kc + ((size_t)kv * p.c_stride + kk) * HD + d0;
+          vs = p.vc + ((size_t)kv * p.c_stride + kk) * HD + d0;
+        } else {
+          ks = p.kt + ((size_t)kv * p.T + (kk - p.C)) * HD + d0;
+          vs = p.vt + ((size_t)kv * p.T + (kk - p.C)) * HD + d0;
+        }
+        kvv = *reinterpret_cast<const u32x4_t*>(ks);
+        vvv = *reinterpret_cast<const u32x4_t*>(vs);
+      }
+      *reinterpret_cast<u32x4_t*>(&k_lds[key * K_STRIDE + d0]) = kvv;
+      const uint32_t vw[4] = {vvv.x, vvv.y, vvv.z, vvv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vt_lds[(d0 + 2 * e) * VT_STRIDE + key] = (uint16_t)(vw[e] & 0xFFFF);
+        vt_lds[(d0 + 2 * e + 1) * VT_STRIDE + key] = (uint16_t)(vw[e] >> 16);
+      }
+    }
+    __syncthreads();
+
+    // ---- S^T tiles: keys (rows) x query rows (cols); two 16-key tiles
+    f32x4_t s[QC][2];
+#pragma unroll
+    for (int c = 0; c < QC; ++c)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) s[c][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int hc = 0; hc < HC; ++hc) {
+        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(&k_lds[(kt * 16 + j) * K_STRIDE + hc * 32 + b * 8]);
+        const bf16x8_t ka = __builtin_bit_cast(bf16x8_t, kf);
+#pragma unroll
+        for (int c = 0; c < QC; ++c)
+          s[c][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[c][hc], s[c][kt], 0, 0, 0);
+      }
+    }
+
+    // ---- mask + online softmax. Lane (j, b) holds keys kt*16 + 4b + e of query row j.
+    const bool tree_tile = (k0 + KT > p.C);
+#pragma unroll
+    for (int c = 0; c < QC; ++c) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int kk = k0 + kt * 16 + 4 * b + e;
+          float v = s[c][kt][e] * p.scale_log2;
+          bool vis = kk < key_end;
+          if (vis && tree_tile && kk >= p.C) {
+            const int jn = kk - p.C;
+            vis = (p.mask[(size_t)qtok[c] * W + (jn >> 6)] >> (jn & 63)) & 1ull;
+          }
+          v = vis ? v : -INFINITY;
+          s[c][kt][e] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run[c], mx);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = exp2f(m_run[c] - m_use);   // exp2(-inf) = 0 on the first tile
+      float psum = 0.f;
+      uint32_t pk[4];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        float pv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pv[e] = exp2f(s[c][kt][e] - m_use);
+          psum += pv[e];
+        }
+        pk[kt * 2 + 0] = pack_bf16x2(pv[0], pv[1]);
+        pk[kt * 2 + 1] = pack_bf16x2(pv[2], pv[3]);
+      }
+      psum += __shfl_xor(psum, 16, 64);
+      psum += __shfl_xor(psum, 32, 64);
+      l_run[c] = l_run[c] * alpha + psum;
+      m_run[c] = m_new;
+#pragma unroll
+      for (int d = 0; d < DT; ++d)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[c][d][e] *= alpha;
+      // P^T operand: lane (j, b) element e' <-> key (e' < 4 ? 4b + e' : 16 + 4b + e' - 4)
+      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
+#pragma unroll
+      for (int d = 0; d < DT; ++d) {
+        // A operand V^T: lane (i = d row, b) element e' <-> same key permutation
+        const uint16_t* vrow = &vt_lds[(d * 16 + j) * VT_STRIDE];
+        const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow + 4 * b);
+        const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + 16 + 4 * b);
+        const bf16x8_t va = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
+        o[c][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[c][d], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- partials: lane (j, b) holds O^T[d = dt*16 + 4b + e][row j]
+#pragma unroll
+  for (int c = 0; c < QC; ++c) {
+    const int r = row_block + c * 16 + j;
+    if (!qvalid[c]) continue;
+    const size_t base = ((size_t)split * p.nkv + kv) * p.rows + r;
+    float* op = p.o_part + base * HD;
+#pragma unroll
+    for (int d = 0; d < DT; ++d)
+      *reinterpret_cast<f32x4_t*>(op + d * 16 + 4 * b) = o[c][d];
+    if (b == 0) {
+      p.ml_part[base * 2 + 0] = m_run[c];
+      p.ml_part[base * 2 + 1] = l_run[c];
+    }
+  }
+}
+
+// Merge the split partials of one (KV head, query row): fixed split order.
+template <int HD>
+__global__ __launch_bounds__(HD) void attn_merge_kernel(AttnParams p, uint16_t* out, float* out_f32) {
+  const int r = blockIdx.x, kv = blockIdx.y, d = threadIdx.x;
+  float M = -INFINITY;
+  for (int s = 0; s < p.splits; ++s)
+    M = fmaxf(M, p.ml_part[(((size_t)s * p.nkv + kv) * p.rows + r) * 2]);
+  const float Mu = (M == -INFINITY) ? 0.f : M;
+  float L = 0.f, acc = 0.f;
+  for (int s = 0; s < p.splits; ++s) {
+    const size_t base = ((size_t)s * p.nkv + kv) * p.rows + r;
+    const float w = exp2f(p.ml_part[base * 2] - Mu);
+    L += w * p.ml_part[base * 2 + 1];
+    acc += w * p.o_part[base * HD + d];
+  }
+  const float v = acc / L;
+  const int t = r / p.grp, h = kv * p.grp + r % p.grp;
+  const size_t o = ((size_t)t * p.nq + h) * HD + d;
+  if (out) out[o] = f32_to_bf16(v);
+  if (out_f32) out_f32[o] = v;
+}
+
+AttnPlan plan_attention(int T, int C, int nq, int nkv, int hd) {
+  AttnPlan pl;
+  const int grp = nq / nkv;
+  const int rows = grp * T;
+  // query-row blocks of 4 waves x QC x 16 rows; QC picked at launch from rows
+  const int qc = (rows <= 64) ? 1 : (rows <= 128) ? 2 : 3;
+  pl.qblocks = (rows + 4 * qc * 16 - 1) / (4 * qc * 16);
+  const int keys = C + T;
+  const int units = pl.qblocks * nkv;
+  // aim for ~256 workgroups, keep >= 4 key tiles per split
+  int splits = std::max(1, 256 / std::max(1, units));
+  const int max_splits = std::max(1, keys / (4 * KT));
+  splits = std::min(splits, max_splits);
+  int kps = (keys + splits - 1) / splits;
+  kps = (kps + KT - 1) / KT * KT;
+  pl.keys_per_split = kps;
+  pl.splits = (keys + kps - 1) / kps;
+  pl.ws_bytes = (size_t)pl.splits * nkv * rows * (hd + 2) * sizeof(float);
+  return pl;
+}
+
+hipError_t launch_attention(const AttnArgs& a, const AttnPlan& pl, void* ws, hipStream_t st) {
+  AttnParams p{};
+  p.q = a.q; p.kc = a.kc; p.vc = a.vc; p.kt = a.kt; p.vt = a.vt; p.mask = a.mask;
+  p.T = a.T; p.C = a.C; p.c_stride = a.c_stride; p.nq = a.nq; p.nkv = a.nkv;
+  p.grp = a.nq / a.nkv;
+  p.rows = p.grp * a.T;
+  p.keys_per_split = pl.keys_per_split;
+  p.splits = pl.splits;
+  p.scale_log2 = a.sm_scale * 1.4426950408889634f;
+  p.o_part = reinterpret_cast<float*>(ws);
+  p.ml_part = p.o_part + (size_t)pl.splits * a.nkv * p.rows * a.hd;
+  const int qc = (p.rows <= 64) ? 1 : (p.rows <= 128) ? 2 : 3;
+  dim3 grid(pl.qblocks, a.nkv, pl.splits);
+  if (a.hd == 128) {
+    if (qc == 1) hipLaunchKernelGGL((tree_attn_kernel<128, 1>), grid, dim3(256), 0, st, p);
+    else if (qc == 2) hipLaunchKernelGGL((tree_attn_kernel<128, 2>), grid, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((tree_attn_kernel<128, 3>), grid, dim3(256), 0, st, p);
+  } else {
+    if (qc == 1) hipLaunchKernelGGL((tree_attn_kernel<64, 1>), grid, dim3(256), 0, st, p);
+    else if (qc == 2) hipLaunchKernelGGL((tree_attn_kernel<64, 2>), grid, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((tree_attn_kernel<64, 3>), grid, dim3(256), 0, st, p);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.hd == 128)
+    hipLaunchKernelGGL((attn_merge_kernel<128>), dim3(p.rows, a.nkv), dim3(128), 0, st, p, a.out, a.out_f32);
+  else
+    hipLaunchKernelGGL((attn_merge_kernel<64>), dim3(p.rows, a.nkv), dim3(64), 0, st, p, a.out, a.out_f32);
+  return hipGetLastError();
+}
+
+}  // namespace ss

@@ -1,0 +1,88 @@
+// Internal launcher interface between the C ABI layer (api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace ss {
+
+enum Epilogue { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+
+struct GemmArgs {
+  const uint16_t* x;   // bf16 [T][K]
+  const uint8_t* qw;   // int4 weights, or null for bf16 weights
+  const uint16_t* sc;
+  const uint16_t* zp;
+  const uint16_t* wb;  // bf16 weights when qw is null
+  int T, N, K;
+  int epi;
+  int swiglu_I;
+  float* y_f32;
+  uint16_t* y_bf16;
+  float* resid;
+  uint16_t* u_bf16;
+};
+
+struct GemmPlan {
+  int row_blocks, tok_blocks, chunks, splits, chunks_per_split;
+  size_t ws_bytes;
+};
+
+GemmPlan plan_gemm(int T, int N, int K, int epi, int swiglu_I);
+hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& pl, void* ws, hipStream_t st);
+
+// quantization
+hipError_t launch_quantize_g64(const uint16_t* w, int64_t n, int64_t k, uint8_t* q, uint16_t* s,
+                               uint16_t* z, hipStream_t st);
+hipError_t launch_dequantize_g64(const uint8_t* q, const uint16_t* s, const uint16_t* z, int64_t n,
+                                 int64_t k, uint16_t* out, hipStream_t st);
+
+// tree + attention
+hipError_t launch_tree_mask(const int32_t* parents, int T, uint64_t* mask, int32_t* depth,
+                            int32_t* err, hipStream_t st);
+
+struct AttnArgs {
+  const uint16_t* q;      // [T][nq][hd]
+  const uint16_t* kc;     // [nkv][c_stride][hd]
+  const uint16_t* vc;
+  const uint16_t* kt;     // [nkv][T][hd]
+  const uint16_t* vt;
+  const uint64_t* mask;   // [T][W]
+  uint16_t* out;          // [T][nq][hd] (nullable)
+  float* out_f32;         // (nullable)
+  int T, C, c_stride, nq, nkv, hd;
+  float sm_scale;
+};
+struct AttnPlan {
+  int splits;             // KV splits of the prefix (the tree part is one more split)
+  int keys_per_split;
+  int qblocks;            // query-row blocks per KV head
+  size_t ws_bytes;
+};
+AttnPlan plan_attention(int T, int C, int nq, int nkv, int hd);
+hipError_t launch_attention(const AttnArgs& a, const AttnPlan& pl, void* ws, hipStream_t st);
+
+// layer glue
+hipError_t launch_embed(const int32_t* tokens, const uint16_t* embed, int T, int H, int V, float* h32,
+                        int32_t* err, hipStream_t st);
+hipError_t launch_bf16_to_f32(const uint16_t* in, size_t n, float* out, hipStream_t st);
+hipError_t launch_f32_to_bf16(const float* in, size_t n, uint16_t* out, hipStream_t st);
+// R output rows; rows (nullable) selects source rows of h32 [src_rows][H]
+hipError_t launch_rmsnorm(const float* h32, const uint16_t* gain, int R, int H, float eps,
+                          uint16_t* out, const int32_t* rows, int src_rows, int32_t* err,
+                          hipStream_t st);
+hipError_t launch_rope_split(const float* qkv, const int32_t* depth, int T, int C, int nq, int nkv,
+                             int hd, float theta, uint16_t* q, uint16_t* kt, uint16_t* vt,
+                             hipStream_t st);
+
+// selection / acceptance
+hipError_t launch_row_argmax(const float* logits, int rows, int vocab, int32_t* out, hipStream_t st);
+hipError_t launch_draft_select(const float* logits, const float* gumbel, int rows, int vocab,
+                               float inv_temp, int k, int32_t* out, hipStream_t st);
+hipError_t launch_tree_accept(const int32_t* parents, const int32_t* tokens, const int32_t* tgt,
+                              int T, int32_t* path, int32_t* len, int32_t* bonus, hipStream_t st);
+
+}  // namespace ss

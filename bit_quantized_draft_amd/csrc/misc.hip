@@ -1,0 +1,347 @@
+// Layer glue (embedding gather, RMSNorm, RoPE + q/k/v scatter), row argmax, draft child
+// selection and the greedy tree-acceptance walk.
+//
+// Acceptance follows greedy token-tree verification (Review page "SubSpec: Using the
+// Target Model's Own Low-Bit Shadow as Its Draft Model", §6.3 and §3.2): from the root,
+// accept the child whose token is the target's argmax at the current node, repeat.
+// Child selection sharpens the draft distribution with a temperature (Summary page
+// "Speculate Deep and Accurate ...", "Approach": 0.2) and keeps k = 6 children per node
+// (Review §6.3); read as Gumbel-top-k sampling without replacement.
+#include "common.h"
+#include "kernels.h"
+
+namespace ss {
+
+// ------------------------------------------------------------------ glue
+
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tokens,
+                                                    const uint16_t* __restrict__ embed, int T, int H,
+                                                    int V, float* __restrict__ h32,
+                                                    int32_t* __restrict__ err) {
+  const int t = blockIdx.x;
+  const int tok = tokens[t];
+  const bool ok = tok >= 0 && tok < V;
+  if (!ok && threadIdx.x == 0 && err) atomicOr(err, 2);
+  for (int i = threadIdx.x; i < H; i += blockDim.x)
+    h32[(size_t)t * H + i] = ok ? bf16_to_f32(embed[(size_t)tok * H + i]) : 0.f;
+}
+
+__global__ __launch_bounds__(256) void bf16_to_f32_kernel(const uint16_t* __restrict__ in, size_t n,
+                                                          float* __restrict__ out) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    out[i] = bf16_to_f32(in[i]);
+}
+
+__global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restrict__ in, size_t n,
+                                                          uint16_t* __restrict__ out) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    out[i] = f32_to_bf16(in[i]);
+}
+
+// out[r] = bf16(h[row] * rsqrt(mean(h[row]^2) + eps) * gain), one workgroup per output row.
+// H % 4 == 0; each thread keeps up to RMS_CACHE float4s of its row in registers (one read
+// of h for H <= 256 * 4 * RMS_CACHE), re-reading only beyond that.
+constexpr int RMS_CACHE = 8;
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ h32,
+                                                      const uint16_t* __restrict__ gain, int H,
+                                                      float eps, uint16_t* __restrict__ out,
+                                                      const int32_t* __restrict__ rows, int src_rows,
+                                                      int32_t* __restrict__ err) {
+  __shared__ float red[4];
+  const int r = blockIdx.x;
+  const int row = rows ? rows[r] : r;
+  const int H4 = H >> 2;
+  uint2* o4 = reinterpret_cast<uint2*>(out + (size_t)r * H);
+  if (row < 0 || row >= src_rows) {   // invalid row index: zeros, error word
+    if (threadIdx.x == 0 && err) atomicOr(err, 4);
+    for (int i = threadIdx.x; i < H4; i += blockDim.x) o4[i] = uint2{0u, 0u};
+    return;
+  }
+  const float4* x4 = reinterpret_cast<const float4*>(h32 + (size_t)row * H);
+  float4 cache[RMS_CACHE];
+  float ss = 0.f;
+#pragma unroll
+  for (int u = 0; u < RMS_CACHE; ++u) {
+    const int i = u * 256 + threadIdx.x;
+    cache[u] = (i < H4) ? x4[i] : float4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int u = 0; u < RMS_CACHE; ++u)
+    ss += cache[u].x * cache[u].x + cache[u].y * cache[u].y + cache[u].z * cache[u].z + cache[u].w * cache[u].w;
+  for (int i = RMS_CACHE * 256 + threadIdx.x; i < H4; i += 256) {
+    const float4 v = x4[i];
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = red[0] + red[1] + red[2] + red[3];
+  const float rs = 1.0f / sqrtf(tot / (float)H + eps);
+  const uint2* g4 = reinterpret_cast<const uint2*>(gain);
+  auto emit = [&](int i, float4 v) {
+    const uint2 g = g4[i];
+    o4[i] = uint2{pack_bf16x2(v.x * rs * bf16lo_to_f32(g.x), v.y * rs * bf16hi_to_f32(g.x)),
+                  pack_bf16x2(v.z * rs * bf16lo_to_f32(g.y), v.w * rs * bf16hi_to_f32(g.y))};
+  };
+#pragma unroll
+  for (int u = 0; u < RMS_CACHE; ++u) {
+    const int i = u * 256 + threadIdx.x;
+    if (i < H4) emit(i, cache[u]);
+  }
+  for (int i = RMS_CACHE * 256 + threadIdx.x; i < H4; i += 256) emit(i, x4[i]);
+}
+
+// qkv fp32 [T][(nq+2nkv)*hd] -> q bf16 [T][nq][hd] and tree K/V bf16 [nkv][T][hd].
+// RoPE (rotate-half) on q and k at position C + depth[t]; angles in fp64.
+__global__ __launch_bounds__(256) void rope_split_kernel(const float* __restrict__ qkv,
+                                                         const int32_t* __restrict__ depth, int T,
+                                                         int C, int nq, int nkv, int hd,
+                                                         double theta, uint16_t* __restrict__ q,
+                                                         uint16_t* __restrict__ kt,
+                                                         uint16_t* __restrict__ vt) {
+  __shared__ float cs[64], sn[64];   // hd <= 128
+  const int t = blockIdx.x;
+  const int half = hd >> 1;
+  const int width = (nq + 2 * nkv) * hd;
+  const double pos = (double)(C + depth[t]);
+  if (threadIdx.x < half) {
+    const double inv = pow(theta, -2.0 * (double)threadIdx.x / (double)hd);
+    double sd, cd;
+    sincos(pos * inv, &sd, &cd);
+    cs[threadIdx.x] = (float)cd;
+    sn[threadIdx.x] = (float)sd;
+  }
+  __syncthreads();
+  const float* row = qkv + (size_t)t * width;
+  for (int e = threadIdx.x; e < (nq + nkv) * half; e += blockDim.x) {
+    const int h = e / half, i = e - h * half;
+    const float c = cs[i], s = sn[i];
+    const float a = row[h * hd + i], bb = row[h * hd + i + half];
+    const float r0 = a * c - bb * s;
+    const float r1 = bb * c + a * s;
+    uint16_t* dst = (h < nq) ? q + ((size_t)t * nq + h) * hd : kt + ((size_t)(h - nq) * T + t) * hd;
+    dst[i] = f32_to_bf16(r0);
+    dst[i + half] = f32_to_bf16(r1);
+  }
+  for (int i = threadIdx.x; i < nkv * hd; i += blockDim.x) {
+    const int kh = i / hd, d = i % hd;
+    vt[((size_t)kh * T + t) * hd + d] = f32_to_bf16(row[(nq + nkv) * hd + i]);
+  }
+}
+
+hipError_t launch_embed(const int32_t* tokens, const uint16_t* embed, int T, int H, int V, float* h32,
+                        int32_t* err, hipStream_t st) {
+  hipLaunchKernelGGL(embed_kernel, dim3(T), dim3(256), 0, st, tokens, embed, T, H, V, h32, err);
+  return hipGetLastError();
+}
+hipError_t launch_bf16_to_f32(const uint16_t* in, size_t n, float* out, hipStream_t st) {
+  const int blocks = (int)std::min<size_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(bf16_to_f32_kernel, dim3(blocks), dim3(256), 0, st, in, n, out);
+  return hipGetLastError();
+}
+hipError_t launch_f32_to_bf16(const float* in, size_t n, uint16_t* out, hipStream_t st) {
+  const int blocks = (int)std::min<size_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(f32_to_bf16_kernel, dim3(blocks), dim3(256), 0, st, in, n, out);
+  return hipGetLastError();
+}
+hipError_t launch_rmsnorm(const float* h32, const uint16_t* gain, int R, int H, float eps,
+                          uint16_t* out, const int32_t* rows, int src_rows, int32_t* err,
+                          hipStream_t st) {
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(R), dim3(256), 0, st, h32, gain, H, eps, out, rows,
+                     src_rows, err);
+  return hipGetLastError();
+}
+hipError_t launch_rope_split(const float* qkv, const int32_t* depth, int T, int C, int nq, int nkv,
+                             int hd, float theta, uint16_t* q, uint16_t* kt, uint16_t* vt,
+                             hipStream_t st) {
+  hipLaunchKernelGGL(rope_split_kernel, dim3(T), dim3(256), 0, st, qkv, depth, T, C, nq, nkv, hd,
+                     (double)theta, q, kt, vt);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ argmax
+
+struct ArgBest {
+  float v;
+  int i;
+};
+// total order: larger value first, equal values by lower index
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+__device__ __forceinline__ ArgBest block_best(float v, int i) {
+  __shared__ float sv[16];
+  __shared__ int si[16];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(v, o, 64);
+    const int oi = __shfl_xor(i, o, 64);
+    if (better(ov, oi, v, i)) { v = ov; i = oi; }
+  }
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) { sv[w] = v; si[w] = i; }
+  __syncthreads();
+  ArgBest r{sv[0], si[0]};
+  for (int k = 1; k < (int)(blockDim.x >> 6); ++k)
+    if (better(sv[k], si[k], r.v, r.i)) { r.v = sv[k]; r.i = si[k]; }
+  return r;
+}
+
+// Batched loads: each thread has SCAN_U independent float4 (or scalar) loads in flight.
+constexpr int SCAN_THREADS = 1024;
+constexpr int SCAN_U = 4;
+
+template <typename F>
+__device__ __forceinline__ void scan_row(const float* __restrict__ x, const float* __restrict__ g,
+                                         int vocab, float scale, F&& visit) {
+  const bool vec = ((vocab & 3) == 0) && ((reinterpret_cast<uintptr_t>(x) & 15) == 0) &&
+                   (!g || ((reinterpret_cast<uintptr_t>(g) & 15) == 0));
+  if (vec) {
+    const int V4 = vocab >> 2;
+    const float4* x4 = reinterpret_cast<const float4*>(x);
+    const float4* g4 = reinterpret_cast<const float4*>(g);
+    for (int base = threadIdx.x; base < V4; base += SCAN_THREADS * SCAN_U) {
+      float4 v[SCAN_U], n[SCAN_U];
+#pragma unroll
+      for (int u = 0; u < SCAN_U; ++u) {
+        const int i = min(base + u * SCAN_THREADS, V4 - 1);
+        v[u] = x4[i];
+        n[u] = g ? g4[i] : float4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < SCAN_U; ++u) {
+        const int i = base + u * SCAN_THREADS;
+        if (i < V4) {
+          visit(v[u].x * scale + n[u].x, 4 * i + 0);
+          visit(v[u].y * scale + n[u].y, 4 * i + 1);
+          visit(v[u].z * scale + n[u].z, 4 * i + 2);
+          visit(v[u].w * scale + n[u].w, 4 * i + 3);
+        }
+      }
+    }
+  } else {
+    for (int base = threadIdx.x; base < vocab; base += SCAN_THREADS * SCAN_U) {
+      float v[SCAN_U], n[SCAN_U];
+#pragma unroll
+      for (int u = 0; u < SCAN_U; ++u) {
+        const int i = min(base + u * SCAN_THREADS, vocab - 1);
+        v[u] = x[i];
+        n[u] = g ? g[i] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < SCAN_U; ++u) {
+        const int i = base + u * SCAN_THREADS;
+        if (i < vocab) visit(v[u] * scale + n[u], i);
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(SCAN_THREADS) void row_argmax_kernel(const float* __restrict__ logits, int vocab,
+                                                                  int32_t* __restrict__ out) {
+  const float* x = logits + (size_t)blockIdx.x * vocab;
+  float bv = -INFINITY;
+  int bi = 0x7FFFFFFF;
+  // scale 1 and no noise: the visited value is the logit itself (x * 1 + 0 is exact)
+  scan_row(x, nullptr, vocab, 1.0f, [&](float v, int i) {
+    if (better(v, i, bv, bi)) { bv = v; bi = i; }
+  });
+  const ArgBest r = block_best(bv, bi);
+  if (threadIdx.x == 0) out[blockIdx.x] = r.i;
+}
+
+// ------------------------------------------------------------------ draft selection
+
+constexpr int SEL_MAX = 16;
+
+__global__ __launch_bounds__(SCAN_THREADS) void draft_select_kernel(const float* __restrict__ logits,
+                                                                    const float* __restrict__ gumbel,
+                                                                    int vocab, float inv_temp, int k,
+                                                                    int32_t* __restrict__ out) {
+  const size_t off = (size_t)blockIdx.x * vocab;
+  float tv[SEL_MAX];
+  int ti[SEL_MAX];
+#pragma unroll
+  for (int s = 0; s < SEL_MAX; ++s) { tv[s] = -INFINITY; ti[s] = 0x7FFFFFFF; }
+  // y = fp32(fp32(logit * inv_temp) + g): two roundings (the library is built without
+  // contraction); with no noise, y + 0 is y
+  scan_row(logits + off, gumbel ? gumbel + off : nullptr, vocab, inv_temp, [&](float y, int i) {
+    if (!better(y, i, tv[SEL_MAX - 1], ti[SEL_MAX - 1])) return;
+    float cv = y;
+    int ci = i;
+#pragma unroll
+    for (int s = 0; s < SEL_MAX; ++s) {
+      if (better(cv, ci, tv[s], ti[s])) {
+        const float xv = tv[s];
+        const int xi = ti[s];
+        tv[s] = cv; ti[s] = ci;
+        cv = xv; ci = xi;
+      }
+    }
+  });
+  for (int r = 0; r < k; ++r) {
+    const ArgBest w = block_best(tv[0], ti[0]);
+    if (threadIdx.x == 0) out[(size_t)blockIdx.x * k + r] = w.i;
+    if (ti[0] == w.i) {   // the owner pops its head
+#pragma unroll
+      for (int s = 0; s < SEL_MAX - 1; ++s) { tv[s] = tv[s + 1]; ti[s] = ti[s + 1]; }
+      tv[SEL_MAX - 1] = -INFINITY;
+      ti[SEL_MAX - 1] = 0x7FFFFFFF;
+    }
+  }
+}
+
+hipError_t launch_row_argmax(const float* logits, int rows, int vocab, int32_t* out, hipStream_t st) {
+  hipLaunchKernelGGL(row_argmax_kernel, dim3(rows), dim3(SCAN_THREADS), 0, st, logits, vocab, out);
+  return hipGetLastError();
+}
+hipError_t launch_draft_select(const float* logits, const float* gumbel, int rows, int vocab,
+                               float inv_temp, int k, int32_t* out, hipStream_t st) {
+  hipLaunchKernelGGL(draft_select_kernel, dim3(rows), dim3(SCAN_THREADS), 0, st, logits, gumbel, vocab,
+                     inv_temp, k, out);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ acceptance walk
+
+// One wavefront. Each step scans the nodes after `cur` 64 at a time for the first child
+// of `cur` carrying the target's token; `cur` strictly increases, so the walk ends
+// within T steps for any input.
+__global__ __launch_bounds__(64) void tree_accept_kernel(const int32_t* __restrict__ parents,
+                                                         const int32_t* __restrict__ tokens,
+                                                         const int32_t* __restrict__ tgt, int T,
+                                                         int32_t* __restrict__ path,
+                                                         int32_t* __restrict__ len,
+                                                         int32_t* __restrict__ bonus) {
+  const int lane = threadIdx.x;
+  int cur = 0, L = 0;
+  while (true) {
+    const int want = tgt[cur];
+    int found = -1;
+    for (int base = cur + 1; base < T; base += 64) {
+      const int i = base + lane;
+      const bool hit = i < T && parents[i] == cur && tokens[i] == want;
+      const unsigned long long m = __ballot(hit);
+      if (m) { found = base + __ffsll((long long)m) - 1; break; }
+    }
+    if (found < 0) break;
+    if (lane == 0) path[L] = found;
+    ++L;
+    cur = found;
+  }
+  for (int i = L + lane; i < T; i += 64) path[i] = -1;
+  if (lane == 0) {
+    *len = L;
+    *bonus = tgt[cur];
+  }
+}
+
+hipError_t launch_tree_accept(const int32_t* parents, const int32_t* tokens, const int32_t* tgt,
+                              int T, int32_t* path, int32_t* len, int32_t* bonus, hipStream_t st) {
+  hipLaunchKernelGGL(tree_accept_kernel, dim3(1), dim3(64), 0, st, parents, tokens, tgt, T, path, len, bonus);
+  return hipGetLastError();
+}
+
+}  // namespace ss
