@@ -308,7 +308,7 @@ def main():
                    "draft_step_ms": round(ms_draft_step, 4), "verify_ms": round(ms_verify, 4),
                    "draft_step_alg_bytes": int(step_bytes),
                    "draft_step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4)},
-        "roofline": {"kernel": "skinny_gemm_kernel<int4, EPI_SWIGLU> (gate_up 37888x3584, T=64)",
+        "roofline": {"kernel": "w4_gemm_kernel<T=64, int4, EPI_SWIGLU> + sk_reduce_kernel (gate_up 37888x3584, T=64)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profile(gu_bytes),

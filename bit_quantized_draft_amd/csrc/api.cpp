@@ -176,11 +176,12 @@ StepLayout plan_step(const ss_model* m, int T, int C, int R, void* base) {
   L.attn = bp.take<uint16_t>((size_t)T * m->nq * m->hd);
   L.ubuf = bp.take<uint16_t>((size_t)T * m->I);
   size_t g = 0;
-  g = std::max(g, ss::plan_gemm(T, qkvN, m->H, ss::EPI_STORE, 0).ws_bytes);
-  g = std::max(g, ss::plan_gemm(T, m->H, m->nq * m->hd, ss::EPI_RESID, 0).ws_bytes);
-  g = std::max(g, ss::plan_gemm(T, 2 * m->I, m->H, ss::EPI_SWIGLU, m->I).ws_bytes);
-  g = std::max(g, ss::plan_gemm(T, m->H, m->I, ss::EPI_RESID, 0).ws_bytes);
-  if (R > 0 && m->V > 0) g = std::max(g, ss::plan_gemm(R, m->V, m->H, ss::EPI_STORE, 0).ws_bytes);
+  auto need = [&](const ss::GemmPlan& pl) { g = std::max(g, pl.ws_bytes); };
+  need(ss::plan_gemm(T, qkvN, m->H, ss::EPI_STORE, 0));
+  need(ss::plan_gemm(T, m->H, m->nq * m->hd, ss::EPI_RESID, 0));
+  need(ss::plan_gemm(T, 2 * m->I, m->H, ss::EPI_SWIGLU, m->I));
+  need(ss::plan_gemm(T, m->H, m->I, ss::EPI_RESID, 0));
+  if (R > 0 && m->V > 0) need(ss::plan_gemm(R, m->V, m->H, ss::EPI_STORE, 0));
   L.gemm_ws = bp.take<char>(g);
   L.attn_ws = bp.take<char>(ss::plan_attention(T, C, m->nq, m->nkv, m->hd).ws_bytes);
   L.total = bp.off;

@@ -2,35 +2,55 @@
 // token counts of a draft tree (T <= 64 per token block), on gfx950 MFMA.
 //
 // W4A16 path (the substitute linear layer: 4-bit weights, bf16 activations, fp32
-// accumulation). Packed int4 weights stream from HBM with 128-bit loads: lane (j, b) of
-// a wave reads 32 consecutive nibbles (one 64-group half) of weight row j. A nibble q is
-// OR-ed into the mantissa of fp16 1024.0 (0x6400), which is the fp16 value 1024 + q
-// exactly; v_fma_mix_f32 then evaluates (1024 + q) * s + c in fp32 straight from that
-// fp16 half, with c = -(1024 + z) * s precomputed per group, so it yields the exact
-// substitute weight (q - z) * s up to one fp32 rounding. v_cvt_pk_bf16_f32 rounds pairs
-// to bf16 and bf16 MFMA (v_mfma_f32_16x16x32_bf16) accumulates in fp32 across all of K.
-// About 2.4 ALU ops per weight, independent of the token count.
+// accumulation). A nibble q is OR-ed into the mantissa of fp16 1024.0 (0x6400), which
+// is the fp16 value 1024 + q exactly; v_fma_mix_f32 evaluates (1024 + q) * s + c in fp32
+// straight from that fp16 half, with c = -(1024 + z) * s precomputed per group, giving
+// the substitute weight (q - z) * s up to one fp32 rounding. v_cvt_pk_bf16_f32 rounds
+// pairs to bf16 and v_mfma_f32_16x16x32_bf16 accumulates in fp32 across all of K.
+// On gfx950 MFMA and VALU work of one SIMD do not overlap, so the ALU time per weight
+// is the dequantization (about 2.4 VALU ops per weight) plus T/16 MFMA passes.
 //
-// MFMA roles: A = activations (16 tokens x 32 k), B = weights (32 k x 16 rows); lane
-// (j, b) supplies k = 32b + 8m .. 32b + 8m + 7 of the 128-wide chunk to MFMA m, so the
-// activations are staged in LDS in exactly that fragment order. Loads are branch-free
-// (out-of-range rows and tokens read a clamped address and are discarded), which lets
-// the compiler count outstanding loads precisely and keep PF chunks in flight.
+// Workgroup: NWC compute waves (one per SIMD by default; two per SIMD measured slower,
+// an MFMA wave and a VALU wave on one SIMD interfere) and NLD = 2 loader waves.
+//  * Compute wave w works on row group rg = w % RG and K phase ph = w / RG (KS phases,
+//    RG = NWC / KS row groups of 32 weight rows). Each holds PF chunks (128 k) of its own
+//    int4 weights in registers, loaded branch-free with 16-byte loads.
+//  * Loader waves copy, per chunk, the activation fragments and the block rows' fp16
+//    scale / zero pairs global -> LDS with gfx950's direct-to-LDS loads
+//    (global_load_lds_dwordx4 / _dword: no registers, no conversion) into a ring of NS
+//    chunk slots. Hand-off through LDS counters: ready[slot] is the sequence number of
+//    the chunk in the slot, done[slot] counts the compute waves that finished reading it.
+//  * MFMA roles: A = activations (16 tokens x 32 k), B = weights (32 k x 16 rows); lane
+//    (j, b) supplies k = 32 b + 8 m .. +7 of the chunk to k-step m, so a fragment block
+//    [m][token tile] is 1 KB, contiguous by lane: exactly one direct-to-LDS load.
 //
-// bf16-weight path: the same engine with dense bf16 weights (LM head, verify pass).
-//
-// Work split: a workgroup of NW waves owns NW*NR*16 weight rows and all tokens of its
-// token block; waves split rows and share the staged activation chunk. Split-K across
-// workgroups writes fp32 partials that a second kernel sums in fixed order.
+// Work split (data parallel + stream-K): a block is (token block of 64, row block of
+// RG * 32 rows) over all of K, cut into steps of KS chunks. With G workgroups (one per
+// CU), workgroup g first takes whole blocks g, g + G, ... (dp_rounds of them), then an
+// even share of the remaining blocks' steps. A block split between workgroups leaves
+// one fp32 partial per piece; a small second kernel adds them in K order (a fixed
+// order: results do not depend on timing) and runs the epilogue.
 #include "common.h"
 #include "kernels.h"
 
 namespace ss {
 
 constexpr int CHUNK_K = 128;
+#ifndef SS_GEMM_NWC
+#define SS_GEMM_NWC 4
+#endif
+constexpr int NWC = SS_GEMM_NWC;   // compute waves
+constexpr int NLD = 2;   // loader waves
+constexpr int NR = 2;    // 16-row weight tiles per compute wave
+constexpr int NS = 6;    // activation chunk slots in LDS
 
-// 16-byte block blk (k = 8 blk .. 8 blk + 7) of a 128-wide chunk feeds MFMA m = blk % 4
-// from lane group b = blk / 4.
+#ifndef SS_GEMM_MIN_PIECE
+#define SS_GEMM_MIN_PIECE 3
+#endif
+#ifndef SS_GEMM_WGS
+#define SS_GEMM_WGS 256
+#endif
+
 struct GemmParams {
   const uint16_t* x;   // bf16 [T][K]
   const uint8_t* qw;   // int4 [N][K/2]
@@ -38,39 +58,18 @@ struct GemmParams {
   const uint16_t* zp;  // fp16 [N][K/64]
   const uint16_t* wb;  // bf16 [N][K]
   int T, N, K;
-  int chunks_per_split;  // 128-wide K chunks per split
-  int splits;
   int swiglu_I;        // rows [0,I) gate, [I,2I) up
-  float* partial;      // fp32 [splits][T][N] when splits > 1
   float* y_f32;        // [T][N]
   uint16_t* y_bf16;    // [T][N]
   float* resid;        // fp32 [T][N] residual stream (EPI_RESID)
   uint16_t* u_bf16;    // bf16 [T][I] (EPI_SWIGLU)
+  int nchunks, nsteps, tb_count;
+  int G, dp_rounds, sk_first, G_sk;
+  long long sk_units;
+  float* partials;     // [2 G_sk][RG][NR][TT][4][64]
 };
 
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
-
-template <int NR, int NW, int EPI>
-__device__ __forceinline__ int row_of(const GemmParams& p, int wave, int r, int j) {
-  if (EPI == EPI_SWIGLU) {
-    constexpr int HALF = NR / 2;
-    const int base = (blockIdx.x * NW + wave) * HALF * 16;
-    return (r < HALF) ? base + r * 16 + j : p.swiglu_I + base + (r - HALF) * 16 + j;
-  }
-  return (blockIdx.x * NW + wave) * NR * 16 + r * 16 + j;
-}
-
-// Final store of one output element for STORE / RESID.
-template <int EPI>
-__device__ __forceinline__ void store_out(const GemmParams& p, int t, int n, float v) {
-  const size_t o = (size_t)t * p.N + n;
-  if (EPI == EPI_RESID) {
-    p.resid[o] += v;
-  } else {
-    if (p.y_f32) p.y_f32[o] = v;
-    if (p.y_bf16) p.y_bf16[o] = f32_to_bf16(v);
-  }
-}
 
 __device__ __forceinline__ float f16lo(uint32_t x) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(x & 0xFFFFu));
@@ -97,15 +96,14 @@ __device__ __forceinline__ u32x4_t dequant8(uint32_t q, float s, float c) {
   return u32x4_t{pk_bf16(w0, w1), pk_bf16(w2, w3), pk_bf16(w4, w5), pk_bf16(w6, w7)};
 }
 
-// Loader -> compute hand-off through LDS counters. Only LDS ordering is needed: a wave's
-// LDS instructions execute in order, so waiting for its own LDS operations
-// (lgkmcnt(0)) before touching a counter orders them. Release/acquire atomics would
-// also wait for every outstanding global load (vmcnt(0)), draining the weight prefetch
-// each chunk, so the counters use relaxed atomics plus explicit LDS waits.
+// LDS hand-off. Only LDS ordering is needed: a wave's LDS operations complete in order,
+// so waiting for them (lgkmcnt(0)) before touching a counter orders them; relaxed
+// atomics avoid the vmcnt(0) that release/acquire would add (it would drain the
+// weight prefetch every chunk).
 __device__ __forceinline__ void lds_wait() { __builtin_amdgcn_s_waitcnt(0xC07F); }   // lgkmcnt(0)
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
-// Bounded waits on LDS counters. A correct pipeline never comes near the limit; the
+// Bounded waits on LDS counters: a correct pipeline never comes near the limit; the
 // bound guarantees that every wave exits even if it were wrong.
 constexpr int kSpinLimit = 1 << 20;
 __device__ __forceinline__ void wait_eq(int* flag, int want) {
@@ -122,129 +120,268 @@ __device__ __forceinline__ void wait_ge(int* flag, int want) {
   }
   compiler_fence();
 }
+__device__ __forceinline__ void lds_store(int* flag, int v) {
+  __hip_atomic_store(flag, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
 
-// SZV: scale and zero of 4 consecutive chunks (8 groups) arrive in one 16-byte load per
-// row tile (needs K % 512 == 0 and split boundaries on multiples of 4 chunks).
-template <int NR, int TT, int NW, bool INT4, int PF, bool SZV, int EPI>
-__global__ __launch_bounds__((NW + 1) * 64) void skinny_gemm_kernel(GemmParams p) {
-  // Waves 0..NW-1 compute; wave NW streams activation chunks into an NB-deep LDS ring.
-  // The hand-off uses LDS counters instead of workgroup barriers: ready[b] holds the
-  // chunk index last written to buffer b, done[b] counts compute waves that finished
-  // reading it. Compute waves never wait for each other, and their in-order load
-  // counters only track their own weight prefetches.
-  constexpr int NB = 4;              // LDS ring depth
-  constexpr int LA = 2;              // chunks the loader holds in registers
-  static_assert(8 % PF == 0, "the main loop is unrolled by 8 chunks (two scale/zero quads)");
-  __shared__ u32x4_t xfrag[NB][4][TT][64];
-  __shared__ int ready[NB];
-  __shared__ int done[NB];
+// A workgroup's work is a list of segments (block, steps [s0, s1)): its dp_rounds whole
+// blocks g, g + G, ..., then the blocks its stream-K unit range [lo, hi) touches.
+struct SegList {
+  int nd, nsk;         // whole blocks, stream-K segments
+  int sb_lo, s_lo;     // first stream-K block and its first step
+  long long hi;
+};
+
+__device__ __forceinline__ SegList make_segs(const GemmParams& p, int g) {
+  SegList L;
+  L.nd = p.dp_rounds;
+  L.nsk = 0;
+  L.sb_lo = L.s_lo = 0;
+  L.hi = 0;
+  if (g < p.G_sk) {
+    const long long lo = (long long)g * p.sk_units / p.G_sk;
+    L.hi = (long long)(g + 1) * p.sk_units / p.G_sk;
+    if (L.hi > lo) {
+      L.sb_lo = (int)(lo / p.nsteps);
+      L.s_lo = (int)(lo % p.nsteps);
+      L.nsk = (int)((L.hi - 1) / p.nsteps) - L.sb_lo + 1;
+    }
+  }
+  return L;
+}
+
+__device__ __forceinline__ void seg_of(const GemmParams& p, const SegList& L, int g, int k, int& block,
+                                       int& s0, int& s1) {
+  if (k < L.nd) {
+    block = g + k * p.G;
+    s0 = 0;
+    s1 = p.nsteps;
+  } else {
+    const int sb = L.sb_lo + (k - L.nd);
+    block = p.sk_first + sb;
+    s0 = (k == L.nd) ? L.s_lo : 0;
+    s1 = (int)min((long long)p.nsteps, L.hi - (long long)sb * p.nsteps);
+  }
+}
+
+// Prefetch cursor over the segments, each padded to a multiple of PF positions so that
+// position p of every segment uses ring slot p % PF; padding positions (and positions
+// past the last segment) reload the segment's last step, which stays in bounds and is
+// never used.
+struct PCur {
+  int k, pos, len, plen, s0, rb;
+};
+
+template <int PF>
+__device__ __forceinline__ void pcur_set(PCur& c, const GemmParams& p, const SegList& L, int g, int k) {
+  int block, s0, s1;
+  seg_of(p, L, g, k, block, s0, s1);
+  c.k = k;
+  c.pos = 0;
+  c.s0 = s0;
+  c.len = s1 - s0;
+  c.plen = (c.len + PF - 1) / PF * PF;
+  c.rb = block / p.tb_count;
+}
+
+template <int PF>
+__device__ __forceinline__ void pcur_next(PCur& c, const GemmParams& p, const SegList& L, int g) {
+  if (++c.pos < c.plen) return;
+  if (c.k + 1 < L.nd + L.nsk) pcur_set<PF>(c, p, L, g, c.k + 1);
+  else c.pos = c.plen - 1;
+}
+
+// workgroup index that owns stream-K unit u
+__device__ __forceinline__ int sk_owner(const GemmParams& p, long long u) {
+  return (int)(((u + 1) * p.G_sk - 1) / p.sk_units);
+}
+// partial slot of workgroup gk's piece of stream-K block sb (a workgroup's range has a
+// partial piece at most at its first and at its last block)
+__device__ __forceinline__ int sk_slot(const GemmParams& p, int gk, int sb) {
+  const long long lo = (long long)gk * p.sk_units / p.G_sk;
+  return 2 * gk + ((int)(lo / p.nsteps) == sb ? 0 : 1);
+}
+
+template <int EPI, int RG>
+__device__ __forceinline__ int tile_row(const GemmParams& p, int rb, int rg, int r, int j) {
+  if (EPI == EPI_SWIGLU) {
+    const int g = rb * RG * 16 + rg * 16 + j;
+    return r == 0 ? g : p.swiglu_I + g;
+  }
+  return rb * RG * 32 + rg * 32 + r * 16 + j;
+}
+template <int EPI, int RG>
+__device__ __forceinline__ bool tile_valid(const GemmParams& p, int rb, int rg, int r) {
+  if (EPI == EPI_SWIGLU) return rb * RG * 16 + rg * 16 < p.swiglu_I;
+  return rb * RG * 32 + rg * 32 + r * 16 < p.N;   // N is a multiple of 16
+}
+
+// Final values of a wave's tiles -> outputs. Lane (j, b) holds tokens t*16 + 4b + e of
+// row j of each tile.
+template <int TT, int EPI, int RG>
+__device__ __forceinline__ void final_store(const GemmParams& p, const f32x4_t (&acc)[NR][TT], int block,
+                                            int rg, int lane) {
+  const int j = lane & 15, b = lane >> 4;
+  const int tb = block % p.tb_count, rb = block / p.tb_count;
+  if (EPI == EPI_SWIGLU) {
+    if (!tile_valid<EPI, RG>(p, rb, rg, 0)) return;
+    const int g = tile_row<EPI, RG>(p, rb, rg, 0, j);
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tok = tb * 64 + t * 16 + 4 * b + e;
+        if (tok < p.T)
+          p.u_bf16[(size_t)tok * p.swiglu_I + g] = f32_to_bf16(silu_f32(acc[0][t][e]) * acc[1][t][e]);
+      }
+    return;
+  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    if (!tile_valid<EPI, RG>(p, rb, rg, r)) continue;
+    const int n = tile_row<EPI, RG>(p, rb, rg, r, j);
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tok = tb * 64 + t * 16 + 4 * b + e;
+        if (tok >= p.T) continue;
+        const size_t o = (size_t)tok * p.N + n;
+        const float v = acc[r][t][e];
+        if (EPI == EPI_RESID) {
+          p.resid[o] += v;
+        } else {
+          if (p.y_f32) p.y_f32[o] = v;
+          if (p.y_bf16) p.y_bf16[o] = f32_to_bf16(v);
+        }
+      }
+  }
+}
+
+template <int TT, bool INT4, int EPI, int KS, int PF>
+__global__ __launch_bounds__((NWC + NLD) * 64) void w4_gemm_kernel(GemmParams p) {
+  constexpr int RG = NWC / KS;
+  constexpr int NCB = KS > 1 ? RG * (KS - 1) : 1;   // phase-combine buffers
+  constexpr int FRAG = TT * 4;                     // 1 KB fragment blocks per chunk
+  constexpr int ROWS = RG * 32;                    // weight rows of a block
+  constexpr int SZL = INT4 ? 2 * ROWS / 64 : 0;    // scale / zero loads per chunk
+  constexpr int LOADS = FRAG + SZL;                // loader instructions per chunk
+  constexpr int LA = (63 / LOADS) < 3 ? (63 / LOADS) : 3;   // chunks in flight per loader
+  static_assert(ROWS % 64 == 0, "scale / zero staging uses whole waves of rows");
+  static_assert(NS % KS == 0 && NS % NLD == 0, "slot ring must split evenly");
+  __shared__ u32x4_t xfrag[NS][4][TT][64];
+  __shared__ uint32_t szs[NS][2][INT4 ? ROWS : 1];   // per row: fp16 scale pair, zero pair
+  __shared__ f32x4_t comb[NCB][NR][TT][64];
+  __shared__ int ready[NS], done[NS];
+  __shared__ int comb_ready[NCB], comb_done[NCB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int j = lane & 15;       // weight row within a 16-row tile / output column
-  const int b = lane >> 4;       // k lane group
-  const int tok0 = blockIdx.z * 64;
-  const int Tb = min(64, p.T - tok0);
-  const int split = blockIdx.y;
-  const int c_begin = split * p.chunks_per_split;
-  const int c_end = min(p.K / CHUNK_K, c_begin + p.chunks_per_split);
-  const int G = p.K >> 6;
-  const int nchunks = c_end - c_begin;
-  const int c_last = max(c_end - 1, c_begin);
+  const int g = blockIdx.x;
+  const SegList L = make_segs(p, g);
+  const int nsegs = L.nd + L.nsk;
 
-  if (tid < NB) {
+  if (tid < NS) {
     ready[tid] = -1;
     done[tid] = 0;
   }
+  if (tid < NCB) {
+    comb_ready[tid] = 0;
+    comb_done[tid] = 0;
+  }
   __syncthreads();   // the only workgroup barrier
 
-  if (wave == NW) {
-    // ---------------- loader wave. Pass (m, tt) fills fragment block [m][tt] of a chunk:
-    // lane l = 16 b + i loads token tt*16 + i, k = 32 b + 8 m .. +7, so every LDS store
-    // instruction writes one contiguous 1 KB block.
-    constexpr int PASSES = TT * 4;
-    u32x4_t v[LA][PASSES];
+  if (wave >= NWC) {
+    // ---------------- loader wave l copies the chunks with sequence number qc = 2 k + l
+    // (k = 0, 1, ...), keeping LA chunks in flight. Before it waits for a slot to be
+    // released it drains and publishes everything it has issued, so no consumer can be
+    // waiting on a chunk the loader holds back.
+    const int l = wave - NWC;
     const int li = lane & 15, lb = lane >> 4;
-    auto load = [&](int slot, int c) {
-#pragma unroll
-      for (int ps = 0; ps < PASSES; ++ps) {
-        const int m = ps & 3, tt = ps >> 2;
-        const int tl = min(tt * 16 + li, Tb - 1);
-        v[slot][ps] = *reinterpret_cast<const u32x4_t*>(p.x + (size_t)(tok0 + tl) * p.K + c * CHUNK_K +
-                                                        lb * 32 + m * 8);
+    int n = 0;    // chunks issued by this loader
+    int ns = 0;   // chunks published (ready) by this loader
+    int qs = 0;   // steps before the current segment
+    auto publish = [&](int upto) {
+      for (; ns < upto; ++ns) {
+        const int qd = 2 * ns + l;
+        if (lane == 0) lds_store(&ready[qd % NS], qd);
       }
     };
-    auto store = [&](int slot, int bufi) {
+    for (int k = 0; k < nsegs; ++k) {
+      int block, s0, s1;
+      seg_of(p, L, g, k, block, s0, s1);
+      const int tb = block % p.tb_count, rb = block / p.tb_count;
+      for (int st = s0; st < s1; ++st, ++qs) {
 #pragma unroll
-      for (int ps = 0; ps < PASSES; ++ps) {
-        const int m = ps & 3, tt = ps >> 2;
-        const bool live = tt * 16 + li < Tb;       // padded tokens contribute zeros
-        const u32x4_t x = v[slot][ps];
-        xfrag[bufi][m][tt][lane] = u32x4_t{live ? x.x : 0u, live ? x.y : 0u, live ? x.z : 0u, live ? x.w : 0u};
-      }
-    };
+        for (int ph = 0; ph < KS; ++ph) {
+          const int qc = qs * KS + ph;
+          if ((qc & 1) != l) continue;
+          const int slot = qc % NS;
+          if (qc >= NS) {
+            const int need = RG * (qc / NS);   // the previous occupant was read by all its waves
+            if (__hip_atomic_load(&done[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < need) {
+              __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+              publish(n);
+              wait_ge(&done[slot], need);
+            }
+          }
+          const int ch = min(st * KS + ph, p.nchunks - 1);
+          const uint16_t* src = p.x + (size_t)ch * CHUNK_K + lb * 32;
 #pragma unroll
-    for (int a = 0; a < LA; ++a) load(a, min(c_begin + a, c_last));
-    for (int q0 = 0; q0 < nchunks; q0 += LA) {
+          for (int ps = 0; ps < FRAG; ++ps) {
+            const int m = ps & 3, tt = ps >> 2;
+            const int tok = min(tb * 64 + tt * 16 + li, p.T - 1);   // padded tokens: clamped copies
+            __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)tok * p.K + m * 8),
+                                             (__attribute__((address_space(3))) void*)&xfrag[slot][m][tt][0],
+                                             16, 0, 0);
+          }
+          if (INT4) {
+            // scale and zero pairs (groups 2 ch, 2 ch + 1) of the block's rows; row
+            // rl = 32 rg + 16 r + j of the block is lane rl % 64 of load rl / 64
+            const int Gq = p.K >> 6;
 #pragma unroll
-      for (int a = 0; a < LA; ++a) {
-        const int q = q0 + a;
-        if (q < nchunks) {
-          const int bq = q % NB;
-          if (q >= NB) wait_ge(&done[bq], NW * (q / NB));   // chunk q - NB fully read
-          store(a, bq);
-          compiler_fence();
-          lds_wait();                                        // fragment stores done
-          if (lane == 0) __hip_atomic_store(&ready[bq], q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-          load(a, min(c_begin + q + LA, c_last));
+            for (int i = 0; i < ROWS / 64; ++i) {
+              const int rl = i * 64 + lane;
+              const int rgl = rl >> 5, rr = (rl >> 4) & 1, jl = rl & 15;
+              const size_t row = tile_valid<EPI, RG>(p, rb, rgl, rr) ? (size_t)tile_row<EPI, RG>(p, rb, rgl, rr, jl) : 0;
+              __builtin_amdgcn_global_load_lds((const void*)(p.sc + row * Gq + 2 * ch),
+                                               (__attribute__((address_space(3))) void*)&szs[slot][0][i * 64], 4, 0, 0);
+              __builtin_amdgcn_global_load_lds((const void*)(p.zp + row * Gq + 2 * ch),
+                                               (__attribute__((address_space(3))) void*)&szs[slot][1][i * 64], 4, 0, 0);
+            }
+          }
+          ++n;
+          if (n - ns > LA) {
+            // all but the newest LA chunks have landed in LDS
+            __builtin_amdgcn_s_waitcnt(((LA * LOADS) & 0xF) | 0x0F70 | (((LA * LOADS) >> 4) << 14));
+            publish(n - LA);
+          }
         }
       }
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    publish(n);
     return;
   }
 
   // ---------------- compute waves
-  int rows[NR];
-  bool rvalid[NR];
-  size_t rbase[NR];   // element offset of the (clamped) row
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    rows[r] = row_of<NR, NW, EPI>(p, wave, r, j);
-    const int lim = (EPI == EPI_SWIGLU) ? ((r < NR / 2) ? p.swiglu_I : 2 * p.swiglu_I) : p.N;
-    // tiles are 16 rows and N (or I) is a multiple of 16: a tile is all valid or all invalid
-    rvalid[r] = rows[r] < lim;
-    rbase[r] = (size_t)(rvalid[r] ? rows[r] : 0);
-  }
+  const int rg = wave % RG, ph = wave / RG;
+  const int j = lane & 15, b = lane >> 4;
 
-  // ---- weight prefetch ring (PF chunks) and scale/zero ring (per chunk, or per 4 chunks)
-  constexpr int QF = 2;   // scale/zero quads in flight: the next quad's is always loaded
   u32x4_t wreg[PF][NR][INT4 ? 1 : 4];
-  uint32_t szreg[INT4 && !SZV ? PF : 1][NR];   // fp16 scale (low) | zero (high), one chunk
-  u32x4_t sq[QF][NR], zq[QF][NR];               // 8 fp16 scales / zeros = 4 chunks x 2 groups
-  const int c_last4 = c_begin + ((nchunks - 1) >> 2) * 4;
-  auto w_load = [&](int slot, int c) {
+
+  auto w_load = [&](int slot, const PCur& c) {
+    const int ch = min((c.s0 + min(c.pos, c.len - 1)) * KS + ph, p.nchunks - 1);
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
+      const size_t row = tile_valid<EPI, RG>(p, c.rb, rg, r) ? (size_t)tile_row<EPI, RG>(p, c.rb, rg, r, j) : 0;
       if (INT4) {
-        wreg[slot][r][0] = *reinterpret_cast<const u32x4_t*>(p.qw + rbase[r] * (p.K >> 1) + c * 64 + b * 16);
-        if (!SZV) {
-          const size_t gi = rbase[r] * G + 2 * c + (b >> 1);
-          szreg[SZV ? 0 : slot][r] = (uint32_t)p.sc[gi] | ((uint32_t)p.zp[gi] << 16);
-        }
+        wreg[slot][r][0] = *reinterpret_cast<const u32x4_t*>(p.qw + row * (p.K >> 1) + ch * 64 + b * 16);
       } else {
 #pragma unroll
         for (int m = 0; m < 4; ++m)
-          wreg[slot][r][m] = *reinterpret_cast<const u32x4_t*>(p.wb + rbase[r] * p.K + c * CHUNK_K + b * 32 + m * 8);
-      }
-    }
-  };
-  auto sz_load = [&](int qs, int c4) {   // c4: first chunk of a 4-chunk quad
-    if (INT4 && SZV) {
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        sq[qs][r] = *reinterpret_cast<const u32x4_t*>(p.sc + rbase[r] * G + 2 * c4);
-        zq[qs][r] = *reinterpret_cast<const u32x4_t*>(p.zp + rbase[r] * G + 2 * c4);
+          wreg[slot][r][m] = *reinterpret_cast<const u32x4_t*>(p.wb + row * p.K + ch * CHUNK_K + b * 32 + m * 8);
       }
     }
   };
@@ -255,158 +392,170 @@ __global__ __launch_bounds__((NW + 1) * 64) void skinny_gemm_kernel(GemmParams p
 #pragma unroll
     for (int t = 0; t < TT; ++t) acc[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // chunk q of this split: wait for its activation buffer; per k-step m, read the
-  // fragments, dequantize the matching weight words and multiply (few live registers);
-  // release the buffer after the last read
-  auto compute = [&](int slot, int qslot, int q) {
-    const int bq = q % NB;
-    wait_eq(&ready[bq], q);
-    float sf[NR], cf[NR];
-    if (INT4) {
+  // one chunk: wait for its activation slot; per k-step m read the fragments, dequantize
+  // the matching weight word and multiply; release the slot after the last read
+  auto compute = [&](int slot, int step, int qc) {
+    const int xs = qc % NS;
+    wait_eq(&ready[xs], qc);
+    if (step * KS + ph < p.nchunks) {   // uniform; false only past the end of K
+      float sf[NR], cf[NR];
+      if (INT4) {
+        const int sh = (b >> 1) * 16;   // group 2 ch + (b >> 1) of the lane
 #pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        uint32_t sz;
-        if (SZV) {
-          const int q4 = slot & 3;   // chunk within the quad (quads start on multiples of 4)
-          const u32x4_t s4 = sq[qslot][r], z4 = zq[qslot][r];
-          const uint32_t sw = q4 == 0 ? s4.x : q4 == 1 ? s4.y : q4 == 2 ? s4.z : s4.w;
-          const uint32_t zw = q4 == 0 ? z4.x : q4 == 1 ? z4.y : q4 == 2 ? z4.z : z4.w;
-          const int sh = (b >> 1) * 16;   // group 2 c + (b >> 1) of the lane
-          sz = ((sw >> sh) & 0xFFFFu) | (((zw >> sh) & 0xFFFFu) << 16);
-        } else {
-          sz = szreg[SZV ? 0 : slot][r];
+        for (int r = 0; r < NR; ++r) {
+          const int rl = rg * 32 + r * 16 + j;
+          sf[r] = f16lo(szs[xs][0][rl] >> sh);
+          const float zf = f16lo(szs[xs][1][rl] >> sh);
+          cf[r] = __builtin_fmaf(-1024.0f, sf[r], -(zf * sf[r]));   // -(1024 + z) s
         }
-        sf[r] = f16lo(sz);
-        const float zf = f16hi(sz);
-        cf[r] = __builtin_fmaf(-1024.0f, sf[r], -(zf * sf[r]));   // -(1024 + z) s
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      bf16x8_t xa[TT];
-#pragma unroll
-      for (int t = 0; t < TT; ++t) xa[t] = __builtin_bit_cast(bf16x8_t, xfrag[bq][m][t][lane]);
-      if (m == 3) {
-        // the fragment reads have returned (their values are in registers) before the
-        // buffer is released; one increment per wave (atomics run once per active lane)
-        compiler_fence();
-        lds_wait();
-        if (lane == 0) __hip_atomic_fetch_add(&done[bq], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
 #pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        u32x4_t wv;
-        if (INT4) {
-          const u32x4_t w = wreg[slot][r][0];
-          wv = dequant8(m == 0 ? w.x : m == 1 ? w.y : m == 2 ? w.z : w.w, sf[r], cf[r]);
-        } else {
-          wv = wreg[slot][r][m];
+      for (int m = 0; m < 4; ++m) {
+        bf16x8_t xa[TT];
+#pragma unroll
+        for (int t = 0; t < TT; ++t) xa[t] = __builtin_bit_cast(bf16x8_t, xfrag[xs][m][t][lane]);
+        if (m == 3) {
+          // fragment values are in registers before the slot is released; one
+          // increment per wave (atomics run once per active lane)
+          compiler_fence();
+          lds_wait();
+          if (lane == 0) __hip_atomic_fetch_add(&done[xs], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
 #pragma unroll
-        for (int t = 0; t < TT; ++t)
-          acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[t], __builtin_bit_cast(bf16x8_t, wv),
-                                                             acc[r][t], 0, 0, 0);
+        for (int r = 0; r < NR; ++r) {
+          u32x4_t wv;
+          if (INT4) {
+            const u32x4_t w = wreg[slot][r][0];
+            wv = dequant8(m == 0 ? w.x : m == 1 ? w.y : m == 2 ? w.z : w.w, sf[r], cf[r]);
+          } else {
+            wv = wreg[slot][r][m];
+          }
+#pragma unroll
+          for (int t = 0; t < TT; ++t)
+            acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[t], __builtin_bit_cast(bf16x8_t, wv),
+                                                               acc[r][t], 0, 0, 0);
+        }
       }
+    } else {
+      compiler_fence();
+      if (lane == 0) __hip_atomic_fetch_add(&done[xs], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
   };
 
-  // The main loop is unrolled by 8 chunks: weight slot s % PF holds chunk q0 + s, scale
-  // / zero quad slot s / 4 holds chunks q0 + 4 (s / 4) .. +3, so all ring indices are
-  // compile-time registers and the body is straight-line (prefetch indices are clamped
-  // at the end instead of guarded): the load counters stay exact, PF chunks of weights
-  // and the next scale/zero quad stay in flight. A guarded tail handles the last
-  // (chunks mod 8) chunks.
-  constexpr int UNR = 8;
+  // Segments in order; the weight prefetch runs PF positions ahead along the padded
+  // position sequence (across segment boundaries) and is issued unconditionally, so
+  // the load counters stay exact and ring slots are compile-time registers.
+  PCur pc;
+  pcur_set<PF>(pc, p, L, g, 0);
 #pragma unroll
-  for (int s = 0; s < PF; ++s) w_load(s, min(c_begin + s, c_last));
-  sz_load(0, c_begin);
-  sz_load(1, min(c_begin + 4, c_last4));
-  int q0 = 0;
-  for (; q0 + UNR <= nchunks; q0 += UNR) {
-#pragma unroll
-    for (int s = 0; s < UNR; ++s) {
-      const int c = c_begin + q0 + s;
-      compute(s % PF, s >> 2, q0 + s);
-      w_load(s % PF, min(c + PF, c_last));
-      if ((s & 3) == 3) sz_load(s >> 2, min(c + 5, c_last4));   // quad two ahead
-    }
+  for (int u = 0; u < PF; ++u) {
+    w_load(u, pc);
+    pcur_next<PF>(pc, p, L, g);
   }
+  int qs = 0;   // steps before the current segment
+  for (int k = 0; k < nsegs; ++k) {
+    int block, s0, s1;
+    seg_of(p, L, g, k, block, s0, s1);
+    const int len = s1 - s0;
+    for (int p0 = 0; p0 < len; p0 += PF) {
 #pragma unroll
-  for (int s = 0; s < UNR; ++s) {
-    if (q0 + s < nchunks) {
-      const int c = c_begin + q0 + s;
-      compute(s % PF, s >> 2, q0 + s);
-      w_load(s % PF, min(c + PF, c_last));
-      if ((s & 3) == 3) sz_load(s >> 2, min(c + 5, c_last4));
-    }
-  }
-
-  // ---- epilogue: lane holds tokens t*16 + 4b + e of row tile r, column j
-  if (p.splits > 1) {
-    float* part = p.partial + (size_t)split * p.T * p.N;
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      if (!rvalid[r]) continue;
-#pragma unroll
-      for (int t = 0; t < TT; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int tok = t * 16 + 4 * b + e;
-          if (tok < Tb) part[(size_t)(tok0 + tok) * p.N + rows[r]] = acc[r][t][e];
-        }
-    }
-    return;
-  }
-  if (EPI == EPI_SWIGLU) {
-    constexpr int HALF = NR / 2;
-#pragma unroll
-    for (int r = 0; r < HALF; ++r) {
-      if (!rvalid[r]) continue;
-#pragma unroll
-      for (int t = 0; t < TT; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int tok = t * 16 + 4 * b + e;
-          if (tok < Tb) {
-            const float g = acc[r][t][e], u = acc[r + HALF][t][e];
-            p.u_bf16[(size_t)(tok0 + tok) * p.swiglu_I + rows[r]] = f32_to_bf16(silu_f32(g) * u);
-          }
-        }
-    }
-    return;
-  }
-#pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    if (!rvalid[r]) continue;
-#pragma unroll
-    for (int t = 0; t < TT; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int tok = t * 16 + 4 * b + e;
-        if (tok < Tb) store_out<EPI>(p, tok0 + tok, rows[r], acc[r][t][e]);
+      for (int u = 0; u < PF; ++u) {
+        if (p0 + u < len) compute(u, s0 + p0 + u, (qs + p0 + u) * KS + ph);
+        w_load(u, pc);
+        pcur_next<PF>(pc, p, L, g);
       }
+    }
+    qs += len;
+
+    // ---- end of segment: combine the K phases in LDS (fixed order), then store the
+    // result, or the partial of a block split between workgroups
+    if (KS > 1) {
+      if (ph > 0) {
+        const int cb = rg * (KS - 1) + ph - 1;
+        wait_ge(&comb_done[cb], k);
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+          for (int t = 0; t < TT; ++t) comb[cb][r][t][lane] = acc[r][t];
+        compiler_fence();
+        lds_wait();
+        if (lane == 0) lds_store(&comb_ready[cb], k + 1);
+      } else {
+#pragma unroll
+        for (int q = 1; q < KS; ++q) {
+          const int cb = rg * (KS - 1) + q - 1;
+          wait_ge(&comb_ready[cb], k + 1);
+#pragma unroll
+          for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int t = 0; t < TT; ++t) acc[r][t] += comb[cb][r][t][lane];
+          compiler_fence();
+          lds_wait();
+          if (lane == 0) lds_store(&comb_done[cb], k + 1);
+        }
+      }
+    }
+    if (ph == 0) {
+      if (s0 == 0 && s1 == p.nsteps) {
+        final_store<TT, EPI, RG>(p, acc, block, rg, lane);
+      } else {
+        float* part = p.partials + ((size_t)sk_slot(p, g, block - p.sk_first) * RG + rg) * (NR * TT * 4 * 64);
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+          for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) part[((r * TT + t) * 4 + e) * 64 + lane] = acc[r][t][e];
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int t = 0; t < TT; ++t) acc[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 }
 
-// Fixed-order sum of split-K partials followed by the epilogue.
-template <int EPI>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p) {
-  const int ncols = (EPI == EPI_SWIGLU) ? p.swiglu_I : p.N;
-  const size_t total = (size_t)p.T * ncols;
-  const size_t stride = (size_t)p.T * p.N;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
-    const int t = (int)(i / ncols), n = (int)(i % ncols);
-    if (EPI == EPI_SWIGLU) {
-      float g = 0.f, u = 0.f;
-      for (int s = 0; s < p.splits; ++s) {
-        g += p.partial[s * stride + (size_t)t * p.N + n];
-        u += p.partial[s * stride + (size_t)t * p.N + p.swiglu_I + n];
-      }
-      p.u_bf16[(size_t)t * p.swiglu_I + n] = f32_to_bf16(silu_f32(g) * u);
+// Blocks split between workgroups: every thread owns one output element (for SwiGLU,
+// one gate / up pair) of one block, adds the pieces' partials in K order (a fixed
+// order, so results do not depend on timing) and applies the epilogue. A block that
+// one workgroup covered whole was stored by the GEMM kernel itself.
+template <int TT, int EPI, int KS>
+__global__ __launch_bounds__(256) void sk_reduce_kernel(GemmParams p) {
+  constexpr int RG = NWC / KS;
+  constexpr int NRE = (EPI == EPI_SWIGLU) ? 1 : NR;   // tiles handled per thread set
+  constexpr int PER_BLOCK = RG * NRE * TT * 4 * 64;
+  const int sb = blockIdx.x;
+  const int idx = blockIdx.y * 256 + threadIdx.x;
+  if (idx >= PER_BLOCK) return;
+  const long long u0 = (long long)sb * p.nsteps;
+  const int g0 = sk_owner(p, u0), g1 = sk_owner(p, u0 + p.nsteps - 1);
+  if (g0 == g1) return;
+  const int lane = idx & 63;
+  const int e = (idx >> 6) & 3;
+  const int t = (idx >> 8) % TT;
+  const int r = (idx >> 8) / TT % NRE;
+  const int rg = (idx >> 8) / TT / NRE;
+  const int block = p.sk_first + sb;
+  const int tb = block % p.tb_count, rb = block / p.tb_count;
+  const int j = lane & 15, bq = lane >> 4;
+  const int tok = tb * 64 + t * 16 + 4 * bq + e;
+  if (tok >= p.T || !tile_valid<EPI, RG>(p, rb, rg, r)) return;
+  float v0 = 0.f, v1 = 0.f;
+  for (int gk = g0; gk <= g1; ++gk) {
+    const float* part = p.partials + ((size_t)sk_slot(p, gk, sb) * RG + rg) * (NR * TT * 4 * 64);
+    v0 += part[((r * TT + t) * 4 + e) * 64 + lane];
+    if (EPI == EPI_SWIGLU) v1 += part[((1 * TT + t) * 4 + e) * 64 + lane];
+  }
+  const int n = tile_row<EPI, RG>(p, rb, rg, r, j);
+  if (EPI == EPI_SWIGLU) {
+    p.u_bf16[(size_t)tok * p.swiglu_I + n] = f32_to_bf16(silu_f32(v0) * v1);
+  } else {
+    const size_t o = (size_t)tok * p.N + n;
+    if (EPI == EPI_RESID) {
+      p.resid[o] += v0;
     } else {
-      float v = 0.f;
-      for (int s = 0; s < p.splits; ++s) v += p.partial[s * stride + (size_t)t * p.N + n];
-      store_out<EPI>(p, t, n, v);
+      if (p.y_f32) p.y_f32[o] = v0;
+      if (p.y_bf16) p.y_bf16[o] = f32_to_bf16(v0);
     }
   }
 }
@@ -414,70 +563,70 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmParams p) {
 // ------------------------------------------------------------------ host side
 
 namespace {
-#ifndef SS_GEMM_NW
-#define SS_GEMM_NW 4
-#endif
-#ifndef SS_GEMM_NR
-#define SS_GEMM_NR 2
-#endif
 #ifndef SS_GEMM_PF
 #define SS_GEMM_PF 4
 #endif
 #ifndef SS_GEMM_PFB
 #define SS_GEMM_PFB 2
 #endif
-constexpr int kNW = SS_GEMM_NW;   // compute waves per workgroup
-constexpr int kNR = SS_GEMM_NR;   // 16-row weight tiles per compute wave
-constexpr int kPF = SS_GEMM_PF;   // int4 weight chunks in flight per wave (multiple of 4)
-constexpr int kPFB = SS_GEMM_PFB; // bf16 weight chunks in flight per wave
-constexpr int kRowsPerBlock = kNW * kNR * 16;
+#ifndef SS_GEMM_KS
+#define SS_GEMM_KS 1
+#endif
+constexpr int kPF = SS_GEMM_PF;     // int4 weight steps in flight per wave
+constexpr int kPFB = SS_GEMM_PFB;   // bf16 weight steps in flight per wave
 
-int choose_splits(int row_blocks, int chunks, int tok_blocks) {
-  const int target = 256;
-  const int units = std::max(1, row_blocks * tok_blocks);
-  int s = (target + units - 1) / units;
-  s = std::max(1, std::min(s, chunks / 4));
-  return std::max(1, std::min(s, chunks));
-}
-
-template <int TT, bool INT4, bool SZV, int EPI>
-hipError_t launch_tt(const GemmParams& p, dim3 grid, hipStream_t st) {
+template <int TT, bool INT4, int EPI, int KS>
+hipError_t launch_k(const GemmParams& p, int sk_blocks, hipStream_t st) {
   constexpr int PF = INT4 ? kPF : kPFB;
-  hipLaunchKernelGGL((skinny_gemm_kernel<kNR, TT, kNW, INT4, PF, SZV, EPI>), grid, dim3((kNW + 1) * 64), 0, st, p);
+  hipLaunchKernelGGL((w4_gemm_kernel<TT, INT4, EPI, KS, PF>), dim3(p.G), dim3((NWC + NLD) * 64), 0, st, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || sk_blocks == 0) return e;
+  constexpr int per_block = (NWC / KS) * (EPI == EPI_SWIGLU ? 1 : NR) * TT * 4 * 64;
+  hipLaunchKernelGGL((sk_reduce_kernel<TT, EPI, KS>), dim3(sk_blocks, (per_block + 255) / 256), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
-template <bool INT4, bool SZV, int EPI>
-hipError_t launch_tt_any(const GemmParams& p, int TT, dim3 grid, hipStream_t st) {
+template <bool INT4, int EPI, int KS>
+hipError_t launch_tt(const GemmParams& p, int TT, int skb, hipStream_t st) {
   switch (TT) {
-    case 1: return launch_tt<1, INT4, SZV, EPI>(p, grid, st);
-    case 2: return launch_tt<2, INT4, SZV, EPI>(p, grid, st);
-    case 3: return launch_tt<3, INT4, SZV, EPI>(p, grid, st);
-    default: return launch_tt<4, INT4, SZV, EPI>(p, grid, st);
+    case 1: return launch_k<1, INT4, EPI, KS>(p, skb, st);
+    case 2: return launch_k<2, INT4, EPI, KS>(p, skb, st);
+    case 3: return launch_k<3, INT4, EPI, KS>(p, skb, st);
+    default: return launch_k<4, INT4, EPI, KS>(p, skb, st);
   }
 }
 
 template <int EPI>
-hipError_t launch_epi(const GemmParams& p, bool int4, bool szv, int TT, dim3 grid, hipStream_t st) {
-  if (!int4) return launch_tt_any<false, false, EPI>(p, TT, grid, st);
-  return szv ? launch_tt_any<true, true, EPI>(p, TT, grid, st) : launch_tt_any<true, false, EPI>(p, TT, grid, st);
+hipError_t launch_epi(const GemmParams& p, bool int4, int TT, int KS, int skb, hipStream_t st) {
+  if (KS == 1) return int4 ? launch_tt<true, EPI, 1>(p, TT, skb, st) : launch_tt<false, EPI, 1>(p, TT, skb, st);
+  return int4 ? launch_tt<true, EPI, 2>(p, TT, skb, st) : launch_tt<false, EPI, 2>(p, TT, skb, st);
 }
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 }  // namespace
 
 GemmPlan plan_gemm(int T, int N, int K, int epi, int swiglu_I) {
-  GemmPlan pl;
-  const int rows = (epi == EPI_SWIGLU) ? 2 * swiglu_I : N;
-  const int half_rows = (epi == EPI_SWIGLU) ? swiglu_I : N;
-  const int per_block = (epi == EPI_SWIGLU) ? kRowsPerBlock / 2 : kRowsPerBlock;
-  pl.row_blocks = (half_rows + per_block - 1) / per_block;
-  (void)rows;
-  pl.tok_blocks = (T + 63) / 64;
-  pl.chunks = std::max(1, K / CHUNK_K);
-  pl.splits = choose_splits(pl.row_blocks, pl.chunks, pl.tok_blocks);
-  pl.chunks_per_split = (pl.chunks + pl.splits - 1) / pl.splits;
-  if (pl.chunks % 4 == 0) pl.chunks_per_split = (pl.chunks_per_split + 3) / 4 * 4;   // whole quads
-  pl.splits = (pl.chunks + pl.chunks_per_split - 1) / pl.chunks_per_split;
-  pl.ws_bytes = pl.splits > 1 ? (size_t)pl.splits * T * N * sizeof(float) : 0;
+  GemmPlan pl{};
+  pl.KS = SS_GEMM_KS;
+  const int RG = NWC / pl.KS;
+  pl.TT = (T >= 64) ? 4 : (T + 15) / 16;
+  const int rows_per_block = (epi == EPI_SWIGLU) ? RG * 16 : RG * 32;
+  const int span = (epi == EPI_SWIGLU) ? swiglu_I : N;
+  pl.rb_count = std::max(1, (span + rows_per_block - 1) / rows_per_block);
+  pl.tb_count = std::max(1, (T + 63) / 64);
+  pl.nchunks = std::max(1, K / CHUNK_K);
+  pl.nsteps = (pl.nchunks + pl.KS - 1) / pl.KS;
+  const int blocks = pl.rb_count * pl.tb_count;
+  const int G = SS_GEMM_WGS;
+  pl.dp_rounds = blocks / G;
+  pl.sk_first = pl.dp_rounds * G;
+  pl.sk_blocks = blocks - pl.sk_first;
+  pl.sk_units = (long long)pl.sk_blocks * pl.nsteps;
+  const long long min_piece = std::max(1, SS_GEMM_MIN_PIECE);
+  pl.G_sk = pl.sk_units > 0 ? (int)std::min<long long>(G, std::max<long long>(1, pl.sk_units / min_piece)) : 0;
+  pl.G = pl.dp_rounds > 0 ? G : std::max(1, pl.G_sk);
+  const size_t slot_bytes = (size_t)RG * NR * pl.TT * 4 * 64 * sizeof(float);
+  pl.ws_bytes = pl.sk_blocks > 0 ? align256(2 * (size_t)pl.G_sk * slot_bytes) : 0;
   return pl;
 }
 
@@ -485,32 +634,23 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& pl, void* ws, hipStrea
   GemmParams p{};
   p.x = a.x; p.qw = a.qw; p.sc = a.sc; p.zp = a.zp; p.wb = a.wb;
   p.T = a.T; p.N = a.N; p.K = a.K;
-  p.chunks_per_split = pl.chunks_per_split;
-  p.splits = pl.splits;
   p.swiglu_I = a.swiglu_I;
-  p.partial = reinterpret_cast<float*>(ws);
   p.y_f32 = a.y_f32; p.y_bf16 = a.y_bf16; p.resid = a.resid; p.u_bf16 = a.u_bf16;
-  dim3 grid(pl.row_blocks, pl.splits, pl.tok_blocks);
-  const int TT = (a.T >= 64) ? 4 : (a.T + 15) / 16;
+  p.nchunks = pl.nchunks;
+  p.nsteps = pl.nsteps;
+  p.tb_count = pl.tb_count;
+  p.G = pl.G;
+  p.dp_rounds = pl.dp_rounds;
+  p.sk_first = pl.sk_first;
+  p.G_sk = pl.G_sk;
+  p.sk_units = pl.sk_units;
+  p.partials = pl.sk_blocks > 0 ? reinterpret_cast<float*>(ws) : nullptr;
   const bool int4 = a.qw != nullptr;
-  hipError_t e;
-  // vector scale/zero loads: 16-byte aligned quads of groups and whole quads per split
-  const bool szv = int4 && (a.K % 512 == 0) && (pl.chunks_per_split % 4 == 0);
   switch (a.epi) {
-    case EPI_RESID: e = launch_epi<EPI_RESID>(p, int4, szv, TT, grid, st); break;
-    case EPI_SWIGLU: e = launch_epi<EPI_SWIGLU>(p, int4, szv, TT, grid, st); break;
-    default: e = launch_epi<EPI_STORE>(p, int4, szv, TT, grid, st); break;
+    case EPI_RESID: return launch_epi<EPI_RESID>(p, int4, pl.TT, pl.KS, pl.sk_blocks, st);
+    case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(p, int4, pl.TT, pl.KS, pl.sk_blocks, st);
+    default: return launch_epi<EPI_STORE>(p, int4, pl.TT, pl.KS, pl.sk_blocks, st);
   }
-  if (e != hipSuccess || pl.splits == 1) return e;
-  const int ncols = (a.epi == EPI_SWIGLU) ? a.swiglu_I : a.N;
-  const size_t total = (size_t)a.T * ncols;
-  const int blocks = (int)std::min<size_t>((total + 255) / 256, 4096);
-  switch (a.epi) {
-    case EPI_RESID: hipLaunchKernelGGL(splitk_reduce_kernel<EPI_RESID>, dim3(blocks), dim3(256), 0, st, p); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL(splitk_reduce_kernel<EPI_SWIGLU>, dim3(blocks), dim3(256), 0, st, p); break;
-    default: hipLaunchKernelGGL(splitk_reduce_kernel<EPI_STORE>, dim3(blocks), dim3(256), 0, st, p); break;
-  }
-  return hipGetLastError();
 }
 
 }  // namespace ss

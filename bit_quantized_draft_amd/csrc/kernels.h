@@ -26,9 +26,15 @@ struct GemmArgs {
   uint16_t* u_bf16;
 };
 
+// Decomposition of one GEMM call: row blocks x token blocks, each cut into steps of KS
+// 128-wide K chunks; whole blocks first (dp_rounds per workgroup), the rest split
+// evenly (stream-K) over G_sk workgroups.
 struct GemmPlan {
-  int row_blocks, tok_blocks, chunks, splits, chunks_per_split;
-  size_t ws_bytes;
+  int KS, TT;
+  int rb_count, tb_count, nchunks, nsteps;
+  int G, dp_rounds, sk_first, sk_blocks, G_sk;
+  long long sk_units;
+  size_t ws_bytes;         // partials of split blocks (0 when no block is split)
 };
 
 GemmPlan plan_gemm(int T, int N, int K, int epi, int swiglu_I);

@@ -77,7 +77,8 @@ ss_status ss_dequantize_substitute(const void* qweight, const void* scale, const
  * all T tree tokens at once, bf16 X [T][k], int4 W as above, fp32 accumulation.
  * Outputs (at least one): y_bf16 [T][n] (round-to-nearest-even of the fp32 result)
  * and/or y_f32 [T][n]. 1 <= T <= 256, k % 128 == 0, n % 16 == 0.
- * The workspace holds split-K partial sums; query its size first (may be 0).
+ * The workspace holds the fp32 partial sums of K ranges split between workgroups;
+ * query its size first (may be 0). Its contents need no initialisation.
  * ------------------------------------------------------------------------------ */
 size_t ss_w4a16_linear_workspace(int32_t T, int64_t n, int64_t k);
 ss_status ss_w4a16_linear(const void* x_bf16, int32_t T, const void* qweight, const void* scale,

@@ -1,8 +1,9 @@
 """Parity of the whole substitute-draft step (ss_draft_tree_step) with the oracle.
 
 One layer is compared with the oracle's fp64 layer from the same bf16 hidden input
-(tolerance: rel-L2 <= 1e-2, max-abs <= 2e-2 * max(1, rms(ref))); the tree K/V it writes
-are compared too. Small stacks with an LM head are compared end to end, including the
+(tolerance: rel-L2 <= 1e-2, max-abs <= 2e-2 * max(1, rms(ref)) plus, for outputs stored
+in bf16, the storage rounding of half a bf16 ulp of each reference value); the tree K/V
+it writes are compared too. Small stacks with an LM head are compared end to end, including the
 logits of selected rows.
 """
 
@@ -78,9 +79,9 @@ def test_one_layer_parity(cfgkw, T, C, kind):
     model.draft_tree_step(to_dev(par), C, tk, tv, hidden_in=to_bf16(h_in), hidden_out=hout)
     torch.cuda.synchronize()
     ref_h, ref_k, ref_v = oracle.layer64(oracle.bf16_to_f64(h_in), o_lw, kc, vc, par, C, cfg)
-    assert_close(oracle.bf16_to_f64(bf16_bits(hout)), ref_h, scale_abs=True, what="layer hidden")
-    assert_close(oracle.bf16_to_f64(bf16_bits(tk[0])), ref_k, scale_abs=True, what="tree K")
-    assert_close(oracle.bf16_to_f64(bf16_bits(tv[0])), ref_v, scale_abs=True, what="tree V")
+    assert_close(oracle.bf16_to_f64(bf16_bits(hout)), ref_h, scale_abs=True, bf16_out=True, what="layer hidden")
+    assert_close(oracle.bf16_to_f64(bf16_bits(tk[0])), ref_k, scale_abs=True, bf16_out=True, what="tree K")
+    assert_close(oracle.bf16_to_f64(bf16_bits(tv[0])), ref_v, scale_abs=True, bf16_out=True, what="tree V")
 
 
 @pytest.mark.parametrize("L,T,C,V,kind,rows", [(2, 16, 64, 4096, "R", None),
@@ -108,7 +109,7 @@ def test_small_stack_with_lm_head(L, T, C, V, kind, rows):
     ref_h, ref_lg = oracle.stack64(tok, par, C, embed, [o for o, _, _, _ in layers],
                                    [kc for _, _, kc, _ in layers], [vc for _, _, _, vc in layers],
                                    fnorm, head, cfg, logit_rows=rows)
-    assert_close(oracle.bf16_to_f64(bf16_bits(hout)), ref_h, scale_abs=True, what="stack hidden")
+    assert_close(oracle.bf16_to_f64(bf16_bits(hout)), ref_h, scale_abs=True, bf16_out=True, what="stack hidden")
     assert_close(host(logits), ref_lg, scale_abs=True, what="logits")
 
 
