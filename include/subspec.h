@@ -95,9 +95,9 @@ ss_status ss_w4a16_gate_up_swiglu(const void* x_bf16, int32_t T, const void* qwe
                                   void* u_bf16, void* workspace, size_t ws_bytes, void* stream);
 
 /* Dense bf16-weight linear layer, for layers the draft shares with the target
- * unquantized ([Review] §2.2 step 4: "share whatever layers fit"; the LM head) and for
- * the target verify pass. W bf16 [n][k]; otherwise as ss_w4a16_linear
- * (k % 128 == 0, n % 16 == 0). */
+ * unquantized ([Review] §2.2 step 4: layers that fit on the GPU stay shared with the
+ * target; here the LM head) and for the target verify pass. W bf16 [n][k]; otherwise
+ * as ss_w4a16_linear (k % 128 == 0, n % 16 == 0). */
 size_t ss_bf16_linear_workspace(int32_t T, int64_t n, int64_t k);
 ss_status ss_bf16_linear(const void* x_bf16, int32_t T, const void* w_bf16, int64_t n, int64_t k,
                          void* y_bf16, float* y_f32, void* workspace, size_t ws_bytes,

@@ -3,8 +3,9 @@
 TEST INFRASTRUCTURE ONLY (see the package header).
 
 [Review] §6.2 and [Summary] "Approach" say the substitute layers are data-free,
-training-free 4-bit copies of the target's own layers (named HQQ); [Abstract] calls
-them "low-bit quantized substitute layers". No page gives the quantizer's steps,
+training-free 4-bit copies of the target's own layers (named HQQ); [Abstract]
+describes them as low-bit quantized stand-ins for the offloaded layers. No page gives
+the quantizer's steps,
 group size or zero format, so this oracle takes the plainest reading of a data-free
 4-bit quantizer: asymmetric min-max round-to-nearest per group of 64 consecutive
 input features, with fp16 scale and fp16 (real-valued) zero.
