@@ -65,7 +65,8 @@ hipError_t launch_tree_mask(const int32_t* parents, int T, uint64_t* mask, int32
 // ------------------------------------------------------------------ attention
 
 constexpr int KT = 32;                 // keys per tile
-constexpr int VT_STRIDE = KT + 4;      // halfs per transposed-V row (72 B, 8-B aligned)
+constexpr int VT_STRIDE = KT + 2;      // halfs per transposed-V row: 17 words, so the
+                                       // key-pair writes of a wave hit distinct banks
 
 struct AttnParams {
   const uint16_t* q;
@@ -87,8 +88,8 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnParams p) {
   constexpr int HC = HD / 32;               // 32-wide hd chunks
   constexpr int DT = HD / 16;               // 16-wide d tiles of the output
   constexpr int K_STRIDE = HD + 8;          // halfs per K row in LDS (pad against bank conflicts)
-  __shared__ __align__(16) uint16_t k_lds[KT * K_STRIDE];
-  __shared__ __align__(16) uint16_t vt_lds[HD * VT_STRIDE];
+  __shared__ __align__(16) uint16_t k_lds[2][KT * K_STRIDE];
+  __shared__ __align__(16) uint16_t vt_lds[2][HD * VT_STRIDE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 15, b = lane >> 4;
@@ -128,34 +129,72 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnParams p) {
     for (int d = 0; d < DT; ++d) o[c][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  for (int k0 = key_begin; k0 < key_end; k0 += KT) {
-    // ---- stage K tile [KT][HD] and V^T tile [HD][KT]
-    constexpr int CHUNKS = KT * HD / 8;     // 16-byte chunks per tile
-    for (int ci = tid; ci < CHUNKS; ci += NW * 64) {
+  // ---- K / V tile staging, software-pipelined: the next tile's global loads are issued
+  // before the current tile is computed and land in the other LDS buffer afterwards.
+  // K: thread -> (key, 8-wide hd chunk), 16-byte rows. V: thread -> (key pair, 8-wide hd
+  // chunk); the pair is written transposed as 4-byte words vt[d][key, key + 1], lanes of a
+  // wave covering 8 key pairs x 8 hd chunks (bank-conflict free with 17-word rows).
+  constexpr int KCH = KT * HD / 8 / (NW * 64);        // K chunks per thread
+  constexpr int VU = (KT / 2) * (HD / 8);              // V key-pair chunks per tile
+  static_assert(KCH >= 1 && VU <= NW * 64 && KT == 32, "tile / workgroup shape");
+  const bool v_owner = tid < VU;                       // whole waves (VU is 128 or 256)
+  u32x4_t kreg[KCH], vreg[2];
+  auto key_src = [&](int kk, const uint16_t* cache, const uint16_t* tree, int d0) -> const uint16_t* {
+    return kk < p.C ? cache + ((size_t)kv * p.c_stride + kk) * HD + d0
+                    : tree + ((size_t)kv * p.T + (kk - p.C)) * HD + d0;
+  };
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int ci = tid + i * NW * 64;
       const int key = ci / (HD / 8), d0 = (ci % (HD / 8)) * 8;
       const int kk = k0 + key;
-      u32x4_t kvv = {0u, 0u, 0u, 0u}, vvv = {0u, 0u, 0u, 0u};
-      if (kk < key_end) {
-        const uint16_t *ks, *vs;
-        if (kk < p.C) {
-          ks = p.kc + ((size_t)kv * p.c_stride + kk) * HD + d0;
-          vs = p.vc + ((size_t)kv * p.c_stride + kk) * HD + d0;
-        } else {
-          ks = p.kt + ((size_t)kv * p.T + (kk - p.C)) * HD + d0;
-          vs = p.vt + ((size_t)kv * p.T + (kk - p.C)) * HD + d0;
-        }
-        kvv = *reinterpret_cast<const u32x4_t*>(ks);
-        vvv = *reinterpret_cast<const u32x4_t*>(vs);
-      }
-      *reinterpret_cast<u32x4_t*>(&k_lds[key * K_STRIDE + d0]) = kvv;
-      const uint32_t vw[4] = {vvv.x, vvv.y, vvv.z, vvv.w};
+      kreg[i] = kk < key_end ? *reinterpret_cast<const u32x4_t*>(key_src(kk, p.kc, p.kt, d0)) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+    if (v_owner) {
+      const int w = tid >> 6, l = tid & 63;
+      const int kp = (l & 7) + 8 * (w & 1), dc = (l >> 3) + 8 * (w >> 1);
+      const int kk = k0 + 2 * kp;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        vreg[h] = kk + h < key_end ? *reinterpret_cast<const u32x4_t*>(key_src(kk + h, p.vc, p.vt, dc * 8))
+                                   : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < KCH; ++i) {
+      const int ci = tid + i * NW * 64;
+      const int key = ci / (HD / 8), d0 = (ci % (HD / 8)) * 8;
+      *reinterpret_cast<u32x4_t*>(&k_lds[buf][key * K_STRIDE + d0]) = kreg[i];
+    }
+    if (v_owner) {
+      const int w = tid >> 6, l = tid & 63;
+      const int kp = (l & 7) + 8 * (w & 1), dc = (l >> 3) + 8 * (w >> 1);
+      const uint32_t a[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
+      const uint32_t c[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        vt_lds[(d0 + 2 * e) * VT_STRIDE + key] = (uint16_t)(vw[e] & 0xFFFF);
-        vt_lds[(d0 + 2 * e + 1) * VT_STRIDE + key] = (uint16_t)(vw[e] >> 16);
+        // d = 8 dc + 2e (low halves) and 8 dc + 2e + 1 (high halves) of keys 2kp, 2kp+1
+        uint32_t* row0 = reinterpret_cast<uint32_t*>(&vt_lds[buf][(dc * 8 + 2 * e) * VT_STRIDE]);
+        uint32_t* row1 = reinterpret_cast<uint32_t*>(&vt_lds[buf][(dc * 8 + 2 * e + 1) * VT_STRIDE]);
+        row0[kp] = (a[e] & 0xFFFFu) | (c[e] << 16);
+        row1[kp] = (a[e] >> 16) | (c[e] & 0xFFFF0000u);
       }
     }
-    __syncthreads();
+  };
+
+  int buf = 0;
+  if (key_begin < key_end) {
+    load_tile(key_begin);
+    store_tile(0);
+  }
+  __syncthreads();
+  for (int k0 = key_begin; k0 < key_end; k0 += KT) {
+    const bool has_next = k0 + KT < key_end;
+    if (has_next) load_tile(k0 + KT);
+    const uint16_t* kl = k_lds[buf];
+    const uint16_t* vl = vt_lds[buf];
 
     // ---- S^T tiles: keys (rows) x query rows (cols); two 16-key tiles
     f32x4_t s[QC][2];
@@ -167,7 +206,7 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnParams p) {
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int hc = 0; hc < HC; ++hc) {
-        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(&k_lds[(kt * 16 + j) * K_STRIDE + hc * 32 + b * 8]);
+        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(&kl[(kt * 16 + j) * K_STRIDE + hc * 32 + b * 8]);
         const bf16x8_t ka = __builtin_bit_cast(bf16x8_t, kf);
 #pragma unroll
         for (int c = 0; c < QC; ++c)
@@ -197,9 +236,14 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnParams p) {
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run[c], mx);
+      // Lazy rescaling: the reference max of a row moves only when the tile's max exceeds
+      // it by more than 8 (log2 units), so P stays <= 2^8 and O / l are rescaled only in
+      // the (wave-uniform) case that some row moved.
+      const bool move = mx > m_run[c] + 8.0f;   // always true on a row's first finite tile
+      const float m_new = move ? fmaxf(m_run[c], mx) : m_run[c];
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = exp2f(m_run[c] - m_use);   // exp2(-inf) = 0 on the first tile
+      const bool any_move = __builtin_amdgcn_ballot_w64(move) != 0;
       float psum = 0.f;
       uint32_t pk[4];
 #pragma unroll
@@ -215,25 +259,31 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnParams p) {
       }
       psum += __shfl_xor(psum, 16, 64);
       psum += __shfl_xor(psum, 32, 64);
-      l_run[c] = l_run[c] * alpha + psum;
       m_run[c] = m_new;
+      if (any_move) {
+        l_run[c] = l_run[c] * alpha + psum;
 #pragma unroll
-      for (int d = 0; d < DT; ++d)
+        for (int d = 0; d < DT; ++d)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[c][d][e] *= alpha;
+          for (int e = 0; e < 4; ++e) o[c][d][e] *= alpha;
+      } else {
+        l_run[c] += psum;
+      }
       // P^T operand: lane (j, b) element e' <-> key (e' < 4 ? 4b + e' : 16 + 4b + e' - 4)
       const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
 #pragma unroll
       for (int d = 0; d < DT; ++d) {
         // A operand V^T: lane (i = d row, b) element e' <-> same key permutation
-        const uint16_t* vrow = &vt_lds[(d * 16 + j) * VT_STRIDE];
-        const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow + 4 * b);
-        const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + 16 + 4 * b);
+        const uint32_t* vrow = reinterpret_cast<const uint32_t*>(&vl[(d * 16 + j) * VT_STRIDE]);
+        const u32x2_t lo = {vrow[2 * b], vrow[2 * b + 1]};
+        const u32x2_t hi = {vrow[8 + 2 * b], vrow[8 + 2 * b + 1]};
         const bf16x8_t va = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
         o[c][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[c][d], 0, 0, 0);
       }
     }
+    if (has_next) store_tile(buf ^ 1);   // the other buffer: last read before the previous barrier
     __syncthreads();
+    buf ^= 1;
   }
 
   // ---- partials: lane (j, b) holds O^T[d = dt*16 + 4b + e][row j]
@@ -258,10 +308,12 @@ template <int HD>
 __global__ __launch_bounds__(HD) void attn_merge_kernel(AttnParams p, uint16_t* out, float* out_f32) {
   const int r = blockIdx.x, kv = blockIdx.y, d = threadIdx.x;
   float M = -INFINITY;
+#pragma unroll 8
   for (int s = 0; s < p.splits; ++s)
     M = fmaxf(M, p.ml_part[(((size_t)s * p.nkv + kv) * p.rows + r) * 2]);
   const float Mu = (M == -INFINITY) ? 0.f : M;
   float L = 0.f, acc = 0.f;
+#pragma unroll 8
   for (int s = 0; s < p.splits; ++s) {
     const size_t base = ((size_t)s * p.nkv + kv) * p.rows + r;
     const float w = exp2f(p.ml_part[base * 2] - Mu);
@@ -275,12 +327,20 @@ __global__ __launch_bounds__(HD) void attn_merge_kernel(AttnParams p, uint16_t* 
   if (out_f32) out_f32[o] = v;
 }
 
+// 16-row query tiles per wave. Measured on MI355X: one tile per wave (more workgroups,
+// fewer registers) is fastest up to ~4K keys; long contexts favour three (fewer
+// workgroups re-reading each K/V tile).
+static int attn_qc(int rows, int keys) {
+  const int qc = (rows <= 64) ? 1 : (rows <= 128) ? 2 : 3;
+  return keys <= 4096 ? 1 : qc;
+}
+
 AttnPlan plan_attention(int T, int C, int nq, int nkv, int hd) {
   AttnPlan pl;
   const int grp = nq / nkv;
   const int rows = grp * T;
   // query-row blocks of 4 waves x QC x 16 rows; QC picked at launch from rows
-  const int qc = (rows <= 64) ? 1 : (rows <= 128) ? 2 : 3;
+  const int qc = attn_qc(rows, C + T);
   pl.qblocks = (rows + 4 * qc * 16 - 1) / (4 * qc * 16);
   const int keys = C + T;
   const int units = pl.qblocks * nkv;
@@ -307,7 +367,7 @@ hipError_t launch_attention(const AttnArgs& a, const AttnPlan& pl, void* ws, hip
   p.scale_log2 = a.sm_scale * 1.4426950408889634f;
   p.o_part = reinterpret_cast<float*>(ws);
   p.ml_part = p.o_part + (size_t)pl.splits * a.nkv * p.rows * a.hd;
-  const int qc = (p.rows <= 64) ? 1 : (p.rows <= 128) ? 2 : 3;
+  const int qc = attn_qc(p.rows, a.C + a.T);
   dim3 grid(pl.qblocks, a.nkv, pl.splits);
   if (a.hd == 128) {
     if (qc == 1) hipLaunchKernelGGL((tree_attn_kernel<128, 1>), grid, dim3(256), 0, st, p);

@@ -5,10 +5,11 @@
 // accumulation). A nibble q is OR-ed into the mantissa of fp16 1024.0 (0x6400), which
 // is the fp16 value 1024 + q exactly; v_fma_mix_f32 evaluates (1024 + q) * s + c in fp32
 // straight from that fp16 half, with c = -(1024 + z) * s precomputed per group, giving
-// the substitute weight (q - z) * s up to one fp32 rounding. v_cvt_pk_bf16_f32 rounds
-// pairs to bf16 and v_mfma_f32_16x16x32_bf16 accumulates in fp32 across all of K.
-// On gfx950 MFMA and VALU work of one SIMD do not overlap, so the ALU time per weight
-// is the dequantization (about 2.4 VALU ops per weight) plus T/16 MFMA passes.
+// the substitute weight (q - z) * s up to one fp32 rounding (odd nibbles are masked in
+// place as 1024 + 16 q, see dequant8). v_cvt_pk_bf16_f32 rounds pairs to bf16 and
+// v_mfma_f32_16x16x32_bf16 accumulates in fp32 across all of K. On gfx950 MFMA and VALU
+// work of one SIMD do not overlap, so the ALU time per weight is the dequantization
+// (about 2.1 VALU ops per weight) plus T/16 MFMA passes.
 //
 // Workgroup: NWC compute waves (one per SIMD by default; two per SIMD measured slower,
 // an MFMA wave and a VALU wave on one SIMD interfere) and NLD = 2 loader waves.
@@ -83,16 +84,32 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2v){a, b}, b2v));
 }
 
-// 8 nibbles (k = e, e = 0..7 of one 8-block) -> 8 bf16 weights (q - z) s, natural order
-__device__ __forceinline__ u32x4_t dequant8(uint32_t q, float s, float c) {
-  const uint32_t h04 = (q & 0x000F000Fu) | 0x64006400u;          // 1024+q0 | 1024+q4
-  const uint32_t h15 = ((q >> 4) & 0x000F000Fu) | 0x64006400u;   // q1 | q5
-  const uint32_t h26 = ((q >> 8) & 0x000F000Fu) | 0x64006400u;   // q2 | q6
-  const uint32_t h37 = ((q >> 12) & 0x000F000Fu) | 0x64006400u;  // q3 | q7
+// (a & m) | c in one VOP3 instruction. gfx9 VOP3 encodings take no literal constants, so
+// with both constants written as literals the compiler splits this into v_and + v_or;
+// passing them in registers keeps the single v_and_or_b32.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(c));
+  return r;
+}
+
+// 8 nibbles (k = e, e = 0..7 of one 8-block) -> 8 bf16 weights (q - z) s, natural order.
+// Even nibbles (bits 0-3 of each half) OR-ed into fp16 1024.0 give 1024 + q; odd nibbles
+// (bits 4-7) masked in place give 1024 + 16 q, both exact. With c = -(1024 + z) s and,
+// for the odd ones, s16 = s / 16 and c16 = -(64 + z) s, one fp32 FMA on the fp16 half
+// (v_fma_mix_f32) yields (q - z) s up to one rounding of c; one shift per 32-bit word
+// brings nibbles 2, 3, 6, 7 down.
+__device__ __forceinline__ u32x4_t dequant8(uint32_t q, float s, float c, float s16, float c16) {
+  const uint32_t ME = 0x000F000Fu, MO = 0x00F000F0u, X = 0x64006400u;
+  const uint32_t qh = q >> 8;
+  const uint32_t h04 = and_or(q, ME, X);     // 1024 + q0      | 1024 + q4
+  const uint32_t h15 = and_or(q, MO, X);     // 1024 + 16 q1   | 1024 + 16 q5
+  const uint32_t h26 = and_or(qh, ME, X);    // 1024 + q2      | 1024 + q6
+  const uint32_t h37 = and_or(qh, MO, X);    // 1024 + 16 q3   | 1024 + 16 q7
   const float w0 = __builtin_fmaf(f16lo(h04), s, c), w4 = __builtin_fmaf(f16hi(h04), s, c);
-  const float w1 = __builtin_fmaf(f16lo(h15), s, c), w5 = __builtin_fmaf(f16hi(h15), s, c);
+  const float w1 = __builtin_fmaf(f16lo(h15), s16, c16), w5 = __builtin_fmaf(f16hi(h15), s16, c16);
   const float w2 = __builtin_fmaf(f16lo(h26), s, c), w6 = __builtin_fmaf(f16hi(h26), s, c);
-  const float w3 = __builtin_fmaf(f16lo(h37), s, c), w7 = __builtin_fmaf(f16hi(h37), s, c);
+  const float w3 = __builtin_fmaf(f16lo(h37), s16, c16), w7 = __builtin_fmaf(f16hi(h37), s16, c16);
   return u32x4_t{pk_bf16(w0, w1), pk_bf16(w2, w3), pk_bf16(w4, w5), pk_bf16(w6, w7)};
 }
 
@@ -398,7 +415,7 @@ __global__ __launch_bounds__((NWC + NLD) * 64) void w4_gemm_kernel(GemmParams p)
     const int xs = qc % NS;
     wait_eq(&ready[xs], qc);
     if (step * KS + ph < p.nchunks) {   // uniform; false only past the end of K
-      float sf[NR], cf[NR];
+      float sf[NR], cf[NR], sf16[NR], cf16[NR];
       if (INT4) {
         const int sh = (b >> 1) * 16;   // group 2 ch + (b >> 1) of the lane
 #pragma unroll
@@ -406,7 +423,9 @@ __global__ __launch_bounds__((NWC + NLD) * 64) void w4_gemm_kernel(GemmParams p)
           const int rl = rg * 32 + r * 16 + j;
           sf[r] = f16lo(szs[xs][0][rl] >> sh);
           const float zf = f16lo(szs[xs][1][rl] >> sh);
-          cf[r] = __builtin_fmaf(-1024.0f, sf[r], -(zf * sf[r]));   // -(1024 + z) s
+          cf[r] = -(1024.0f + zf) * sf[r];   // 1024 + z is exact in fp32
+          sf16[r] = sf[r] * 0.0625f;         // exact
+          cf16[r] = -(64.0f + zf) * sf[r];
         }
       }
 #pragma unroll
@@ -426,7 +445,7 @@ __global__ __launch_bounds__((NWC + NLD) * 64) void w4_gemm_kernel(GemmParams p)
           u32x4_t wv;
           if (INT4) {
             const u32x4_t w = wreg[slot][r][0];
-            wv = dequant8(m == 0 ? w.x : m == 1 ? w.y : m == 2 ? w.z : w.w, sf[r], cf[r]);
+            wv = dequant8(m == 0 ? w.x : m == 1 ? w.y : m == 2 ? w.z : w.w, sf[r], cf[r], sf16[r], cf16[r]);
           } else {
             wv = wreg[slot][r][m];
           }
@@ -540,11 +559,30 @@ __global__ __launch_bounds__(256) void sk_reduce_kernel(GemmParams p) {
   const int j = lane & 15, bq = lane >> 4;
   const int tok = tb * 64 + t * 16 + 4 * bq + e;
   if (tok >= p.T || !tile_valid<EPI, RG>(p, rb, rg, r)) return;
+  // piece slots: every piece after the first starts its workgroup's range inside this
+  // block (slot 2 gk); the first piece is its workgroup's first or second block
+  const size_t slot_elems = (size_t)RG * NR * TT * 4 * 64;
+  const size_t off = (size_t)rg * (NR * TT * 4 * 64) + ((r * TT + t) * 4 + e) * 64 + lane;
+  const size_t off1 = (size_t)rg * (NR * TT * 4 * 64) + ((1 * TT + t) * 4 + e) * 64 + lane;
+  auto piece = [&](int gk) { return p.partials + (gk == g0 ? sk_slot(p, g0, sb) : 2 * gk) * slot_elems; };
   float v0 = 0.f, v1 = 0.f;
-  for (int gk = g0; gk <= g1; ++gk) {
-    const float* part = p.partials + ((size_t)sk_slot(p, gk, sb) * RG + rg) * (NR * TT * 4 * 64);
-    v0 += part[((r * TT + t) * 4 + e) * 64 + lane];
-    if (EPI == EPI_SWIGLU) v1 += part[((1 * TT + t) * 4 + e) * 64 + lane];
+  int gk = g0;
+  for (; gk + 4 <= g1 + 1; gk += 4) {   // four independent loads in flight, added in order
+    float a[4], c[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = piece(gk + i)[off];
+      c[i] = EPI == EPI_SWIGLU ? piece(gk + i)[off1] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v0 += a[i];
+      v1 += c[i];
+    }
+  }
+  for (; gk <= g1; ++gk) {
+    v0 += piece(gk)[off];
+    if (EPI == EPI_SWIGLU) v1 += piece(gk)[off1];
   }
   const int n = tile_row<EPI, RG>(p, rb, rg, r, j);
   if (EPI == EPI_SWIGLU) {
