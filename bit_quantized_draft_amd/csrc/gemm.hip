@@ -16,10 +16,12 @@
 //  * Compute wave w works on row group rg = w % RG and K phase ph = w / RG (KS phases,
 //    RG = NWC / KS row groups of 32 weight rows). Each holds PF chunks (128 k) of its own
 //    int4 weights in registers, loaded branch-free with 16-byte loads.
-//  * Loader waves copy, per chunk, the activation fragments and the block rows' fp16
-//    scale / zero pairs global -> LDS with gfx950's direct-to-LDS loads
-//    (global_load_lds_dwordx4 / _dword: no registers, no conversion) into a ring of NS
-//    chunk slots. Hand-off through LDS counters: ready[slot] is the sequence number of
+//  * Loader waves copy, per chunk, the activation fragments (and, when K % 512 != 0, the
+//    block rows' fp16 scale / zero pairs) global -> LDS with gfx950's direct-to-LDS
+//    loads (global_load_lds_dwordx4 / _dword: no registers, no conversion) into a ring
+//    of NS chunk slots. Otherwise a third loader wave stages scale / zero per octet of
+//    chunks with 16-byte loads (one cache line per row instead of one per row and chunk:
+//    the address unit, shared with the weight loads, was the bottleneck). Hand-off through LDS counters: ready[slot] is the sequence number of
 //    the chunk in the slot, done[slot] counts the compute waves that finished reading it.
 //  * MFMA roles: A = activations (16 tokens x 32 k), B = weights (32 k x 16 rows); lane
 //    (j, b) supplies k = 32 b + 8 m .. +7 of the chunk to k-step m, so a fragment block
@@ -275,19 +277,25 @@ __device__ __forceinline__ void final_store(const GemmParams& p, const f32x4_t (
   }
 }
 
-template <int TT, bool INT4, int EPI, int KS, int PF>
-__global__ __launch_bounds__((NWC + NLD) * 64) void w4_gemm_kernel(GemmParams p) {
+// SZO: scale / zero staged per octet of chunks (8 chunks = 16 groups, 32 bytes per row
+// per array, 16-byte loads) by one more loader wave into a 2-slot LDS ring, instead of
+// per chunk with 4-byte loads; needs KS == 1 and K % 512 == 0 (16-byte aligned rows).
+template <int TT, bool INT4, int EPI, int KS, int PF, bool SZO>
+__global__ __launch_bounds__((NWC + NLD + 1) * 64) void w4_gemm_kernel(GemmParams p) {
   constexpr int RG = NWC / KS;
   constexpr int NCB = KS > 1 ? RG * (KS - 1) : 1;   // phase-combine buffers
   constexpr int FRAG = TT * 4;                     // 1 KB fragment blocks per chunk
   constexpr int ROWS = RG * 32;                    // weight rows of a block
-  constexpr int SZL = INT4 ? 2 * ROWS / 64 : 0;    // scale / zero loads per chunk
+  static_assert(!SZO || (INT4 && KS == 1), "octet staging: int4, one K phase");
+  constexpr int SZL = (INT4 && !SZO) ? 2 * ROWS / 64 : 0;   // scale / zero loads per chunk
   constexpr int LOADS = FRAG + SZL;                // loader instructions per chunk
   constexpr int LA = (63 / LOADS) < 3 ? (63 / LOADS) : 3;   // chunks in flight per loader
   static_assert(ROWS % 64 == 0, "scale / zero staging uses whole waves of rows");
   static_assert(NS % KS == 0 && NS % NLD == 0, "slot ring must split evenly");
   __shared__ u32x4_t xfrag[NS][4][TT][64];
-  __shared__ uint32_t szs[NS][2][INT4 ? ROWS : 1];   // per row: fp16 scale pair, zero pair
+  __shared__ uint32_t szs[NS][2][(INT4 && !SZO) ? ROWS : 1];   // per row: fp16 scale pair, zero pair
+  __shared__ __align__(16) uint16_t szo[2][2][SZO ? ROWS : 1][16];   // octet ring: [slot][s|z][row][group]
+  __shared__ int oct_ready[2], oct_done[2];
   __shared__ f32x4_t comb[NCB][NR][TT][64];
   __shared__ int ready[NS], done[NS];
   __shared__ int comb_ready[NCB], comb_done[NCB];
@@ -307,7 +315,48 @@ __global__ __launch_bounds__((NWC + NLD) * 64) void w4_gemm_kernel(GemmParams p)
     comb_ready[tid] = 0;
     comb_done[tid] = 0;
   }
+  if (tid < 2) {
+    oct_ready[tid] = -1;
+    oct_done[tid] = 0;
+  }
   __syncthreads();   // the only workgroup barrier
+
+  if (SZO && wave == NWC + NLD) {
+    // ---------------- scale / zero loader: at every octet start in the sequence (chunk a
+    // multiple of 8, or a segment's first chunk) it copies the block rows' 16 scales and
+    // 16 zeros of that octet into slot oseq % 2, after all compute waves left the slot's
+    // previous octet. Load i covers rows 32 i .. 32 i + 31, lane l -> row 32 i + l / 2,
+    // groups 8 (l % 2) .. +7 of the octet (16 bytes; the LDS order is the row order).
+    const int Gq = p.K >> 6;
+    int oseq = 0;
+    for (int k = 0; k < nsegs; ++k) {
+      int block, s0, s1;
+      seg_of(p, L, g, k, block, s0, s1);
+      const int rb = block / p.tb_count;
+      for (int st = s0; st < s1; ++st) {
+        if ((st & 7) != 0 && st != s0) continue;
+        const int slot = oseq & 1;
+        if (oseq >= 2) wait_ge(&oct_done[slot], RG * (oseq >> 1));
+        const int g0 = (st & ~7) * 2;
+#pragma unroll
+        for (int i = 0; i < ROWS / 32; ++i) {
+          const int rl = i * 32 + (lane >> 1);
+          const int rgl = rl >> 5, rr = (rl >> 4) & 1, jl = rl & 15;
+          const size_t row = tile_valid<EPI, RG>(p, rb, rgl, rr) ? (size_t)tile_row<EPI, RG>(p, rb, rgl, rr, jl) : 0;
+          int gi = g0 + 8 * (lane & 1);
+          if (gi + 8 > Gq) gi = 0;   // octet past the end of K: never read, kept in bounds
+          __builtin_amdgcn_global_load_lds((const void*)(p.sc + row * Gq + gi),
+                                           (__attribute__((address_space(3))) void*)&szo[slot][0][i * 32][0], 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((const void*)(p.zp + row * Gq + gi),
+                                           (__attribute__((address_space(3))) void*)&szo[slot][1][i * 32][0], 16, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        if (lane == 0) lds_store(&oct_ready[slot], oseq);
+        ++oseq;
+      }
+    }
+    return;
+  }
 
   if (wave >= NWC) {
     // ---------------- loader wave l copies the chunks with sequence number qc = 2 k + l
@@ -353,7 +402,7 @@ __global__ __launch_bounds__((NWC + NLD) * 64) void w4_gemm_kernel(GemmParams p)
                                              (__attribute__((address_space(3))) void*)&xfrag[slot][m][tt][0],
                                              16, 0, 0);
           }
-          if (INT4) {
+          if (INT4 && !SZO) {
             // scale and zero pairs (groups 2 ch, 2 ch + 1) of the block's rows; row
             // rl = 32 rg + 16 r + j of the block is lane rl % 64 of load rl / 64
             const int Gq = p.K >> 6;
@@ -411,7 +460,7 @@ __global__ __launch_bounds__((NWC + NLD) * 64) void w4_gemm_kernel(GemmParams p)
 
   // one chunk: wait for its activation slot; per k-step m read the fragments, dequantize
   // the matching weight word and multiply; release the slot after the last read
-  auto compute = [&](int slot, int step, int qc) {
+  auto compute = [&](int slot, int step, int qc, int os) {
     const int xs = qc % NS;
     wait_eq(&ready[xs], qc);
     if (step * KS + ph < p.nchunks) {   // uniform; false only past the end of K
@@ -421,25 +470,34 @@ __global__ __launch_bounds__((NWC + NLD) * 64) void w4_gemm_kernel(GemmParams p)
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
           const int rl = rg * 32 + r * 16 + j;
-          sf[r] = f16lo(szs[xs][0][rl] >> sh);
-          const float zf = f16lo(szs[xs][1][rl] >> sh);
+          float zf;
+          if (SZO) {
+            const int gsel = 2 * (step & 7) + (b >> 1);
+            sf[r] = (float)__builtin_bit_cast(_Float16, szo[os][0][rl][gsel]);
+            zf = (float)__builtin_bit_cast(_Float16, szo[os][1][rl][gsel]);
+          } else {
+            sf[r] = f16lo(szs[xs][0][rl] >> sh);
+            zf = f16lo(szs[xs][1][rl] >> sh);
+          }
           cf[r] = -(1024.0f + zf) * sf[r];   // 1024 + z is exact in fp32
           sf16[r] = sf[r] * 0.0625f;         // exact
           cf16[r] = -(64.0f + zf) * sf[r];
         }
       }
+      // all fragments of the chunk first: the slot is released before the math, and the
+      // LDS latency overlaps the first dequantization
+      bf16x8_t xa[4][TT];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int t = 0; t < TT; ++t) xa[m][t] = __builtin_bit_cast(bf16x8_t, xfrag[xs][m][t][lane]);
+      // fragment values are in registers before the slot is released; one increment per
+      // wave (atomics run once per active lane)
+      compiler_fence();
+      lds_wait();
+      if (lane == 0) __hip_atomic_fetch_add(&done[xs], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        bf16x8_t xa[TT];
-#pragma unroll
-        for (int t = 0; t < TT; ++t) xa[t] = __builtin_bit_cast(bf16x8_t, xfrag[xs][m][t][lane]);
-        if (m == 3) {
-          // fragment values are in registers before the slot is released; one
-          // increment per wave (atomics run once per active lane)
-          compiler_fence();
-          lds_wait();
-          if (lane == 0) __hip_atomic_fetch_add(&done[xs], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        }
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
           u32x4_t wv;
@@ -451,7 +509,7 @@ __global__ __launch_bounds__((NWC + NLD) * 64) void w4_gemm_kernel(GemmParams p)
           }
 #pragma unroll
           for (int t = 0; t < TT; ++t)
-            acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[t], __builtin_bit_cast(bf16x8_t, wv),
+            acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[m][t], __builtin_bit_cast(bf16x8_t, wv),
                                                                acc[r][t], 0, 0, 0);
         }
       }
@@ -471,7 +529,20 @@ __global__ __launch_bounds__((NWC + NLD) * 64) void w4_gemm_kernel(GemmParams p)
     w_load(u, pc);
     pcur_next<PF>(pc, p, L, g);
   }
-  int qs = 0;   // steps before the current segment
+  int qs = 0;         // steps before the current segment
+  int oseq = -1;      // scale / zero octet in use (SZO)
+  auto octet = [&](int st, int s0) {
+    if (SZO && ((st & 7) == 0 || st == s0)) {
+      if (oseq >= 0) {
+        // this wave's reads of the old octet have returned before the slot is released
+        compiler_fence();
+        lds_wait();
+        if (lane == 0) __hip_atomic_fetch_add(&oct_done[oseq & 1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+      ++oseq;
+      wait_eq(&oct_ready[oseq & 1], oseq);
+    }
+  };
   for (int k = 0; k < nsegs; ++k) {
     int block, s0, s1;
     seg_of(p, L, g, k, block, s0, s1);
@@ -479,7 +550,10 @@ __global__ __launch_bounds__((NWC + NLD) * 64) void w4_gemm_kernel(GemmParams p)
     for (int p0 = 0; p0 < len; p0 += PF) {
 #pragma unroll
       for (int u = 0; u < PF; ++u) {
-        if (p0 + u < len) compute(u, s0 + p0 + u, (qs + p0 + u) * KS + ph);
+        if (p0 + u < len) {
+          octet(s0 + p0 + u, s0);
+          compute(u, s0 + p0 + u, (qs + p0 + u) * KS + ph, oseq & 1);
+        }
         w_load(u, pc);
         pcur_next<PF>(pc, p, L, g);
       }
@@ -616,7 +690,12 @@ constexpr int kPFB = SS_GEMM_PFB;   // bf16 weight steps in flight per wave
 template <int TT, bool INT4, int EPI, int KS>
 hipError_t launch_k(const GemmParams& p, int sk_blocks, hipStream_t st) {
   constexpr int PF = INT4 ? kPF : kPFB;
-  hipLaunchKernelGGL((w4_gemm_kernel<TT, INT4, EPI, KS, PF>), dim3(p.G), dim3((NWC + NLD) * 64), 0, st, p);
+  constexpr bool CAN_SZO = INT4 && KS == 1;
+  const bool aligned16 = (reinterpret_cast<uintptr_t>(p.sc) % 16 == 0) && (reinterpret_cast<uintptr_t>(p.zp) % 16 == 0);
+  if (CAN_SZO && p.K % 512 == 0 && aligned16)
+    hipLaunchKernelGGL((w4_gemm_kernel<TT, INT4, EPI, KS, PF, CAN_SZO>), dim3(p.G), dim3((NWC + NLD + 1) * 64), 0, st, p);
+  else
+    hipLaunchKernelGGL((w4_gemm_kernel<TT, INT4, EPI, KS, PF, false>), dim3(p.G), dim3((NWC + NLD) * 64), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sk_blocks == 0) return e;
   constexpr int per_block = (NWC / KS) * (EPI == EPI_SWIGLU ? 1 : NR) * TT * 4 * 64;
