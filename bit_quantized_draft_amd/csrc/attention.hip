@@ -24,30 +24,30 @@ namespace ss {
 
 // ------------------------------------------------------------------ tree mask
 
-// One thread per node walks its parent chain (at most T steps). Invalid parents stop
-// the walk and raise the error word, so an invalid tree never reads out of bounds.
-// T <= 256, so a row has at most 4 mask words.
+// T <= 256, so a row has at most 4 mask words; the parent array is staged in LDS.
 __global__ __launch_bounds__(256) void tree_mask_kernel(const int32_t* __restrict__ parents, int T,
                                                         uint64_t* __restrict__ mask,
                                                         int32_t* __restrict__ depth,
                                                         int32_t* __restrict__ err) {
+  __shared__ int par[256];
   const int W = (T + 63) >> 6;
   // this kernel opens every call that uses the error word: clear it first (no memset
   // node, so the call sequence can be captured in a graph)
-  if (err) {
-    if (threadIdx.x == 0) *err = 0;
-    __syncthreads();
-  }
+  if (err && threadIdx.x == 0) *err = 0;
+  for (int i = threadIdx.x; i < T; i += blockDim.x) par[i] = parents[i];
+  __syncthreads();
+  // One thread per node walks its parent chain in LDS (at most T steps). Invalid parents
+  // stop the walk and raise the error word, so an invalid tree never reads out of bounds.
   for (int i = threadIdx.x; i < T; i += blockDim.x) {
     uint64_t words[4] = {0, 0, 0, 0};
     int cur = i, d = 0, steps = 0;
-    bool bad = (i == 0) ? (parents[0] != -1) : false;
+    bool bad = (i == 0) ? (par[0] != -1) : false;
     while (true) {
       words[cur >> 6] |= 1ull << (cur & 63);
       if (cur == 0) break;
-      const int p = parents[cur];
-      if (p < 0 || p >= cur || ++steps > T) { bad = true; break; }
-      cur = p;
+      const int pp = par[cur];
+      if (pp < 0 || pp >= cur || ++steps > T) { bad = true; break; }
+      cur = pp;
       ++d;
     }
     for (int w = 0; w < W; ++w) mask[(size_t)i * W + w] = words[w];
@@ -64,9 +64,11 @@ hipError_t launch_tree_mask(const int32_t* parents, int T, uint64_t* mask, int32
 
 // ------------------------------------------------------------------ attention
 
-constexpr int KT = 32;                 // keys per tile
-constexpr int VT_STRIDE = KT + 2;      // halfs per transposed-V row: 17 words, so the
-                                       // key-pair writes of a wave hit distinct banks
+#ifndef SS_ATTN_NSUB
+#define SS_ATTN_NSUB 2
+#endif
+constexpr int ATT_NSUB = SS_ATTN_NSUB;   // 32-key sub-tiles per K/V tile
+constexpr int ATT_KT = 32 * ATT_NSUB;
 
 struct AttnParams {
   const uint16_t* q;
@@ -82,9 +84,12 @@ struct AttnParams {
   float* ml_part;                          // [splits][nkv][rows][2]  (max in log2 units, sum)
 };
 
-template <int HD, int QC>
+template <int HD, int QC, int NSUB>
 __global__ __launch_bounds__(256) void tree_attn_kernel(AttnParams p) {
   constexpr int NW = 4;
+  constexpr int KT = 32 * NSUB;             // keys per tile: NSUB sub-tiles of 32
+  constexpr int VT_STRIDE = KT + 2;         // halfs per transposed-V row: (KT + 2) / 2 words,
+                                            // odd, so key-pair writes of a wave spread over banks
   constexpr int HC = HD / 32;               // 32-wide hd chunks
   constexpr int DT = HD / 16;               // 16-wide d tiles of the output
   constexpr int K_STRIDE = HD + 8;          // halfs per K row in LDS (pad against bank conflicts)
@@ -96,13 +101,13 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnParams p) {
   const int kv = blockIdx.y;
   const int split = blockIdx.z;
   const int row_block = blockIdx.x * NW * QC * 16 + wave * QC * 16;
-  const int W = (p.T + 63) >> 6;
+  const int W = (p.T + 63) >> 6;   // mask words per row
   const int key_begin = split * p.keys_per_split;
   const int key_end = min(p.C + p.T, key_begin + p.keys_per_split);
 
   // Q fragments (B operand of S^T = K Q^T): lane (j, b) holds Q[row j][hd 8b..8b+7] per chunk
   bf16x8_t qf[QC][HC];
-  int qtok[QC];
+  uint64_t mw0[QC], mw1[QC], mw2[QC], mw3[QC];   // the row's ancestor mask (T <= 256: 4 words)
   bool qvalid[QC];
 #pragma unroll
   for (int c = 0; c < QC; ++c) {
@@ -110,7 +115,11 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnParams p) {
     qvalid[c] = r < p.rows;
     const int t = qvalid[c] ? r / p.grp : 0;
     const int h = kv * p.grp + (qvalid[c] ? r % p.grp : 0);
-    qtok[c] = t;
+    const uint64_t* mr = p.mask + (size_t)t * W;
+    mw0[c] = mr[0];
+    mw1[c] = W > 1 ? mr[1] : 0ull;
+    mw2[c] = W > 2 ? mr[2] : 0ull;
+    mw3[c] = W > 3 ? mr[3] : 0ull;
 #pragma unroll
     for (int hc = 0; hc < HC; ++hc) {
       u32x4_t v = {0u, 0u, 0u, 0u};
@@ -132,16 +141,28 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnParams p) {
   // ---- K / V tile staging, software-pipelined: the next tile's global loads are issued
   // before the current tile is computed and land in the other LDS buffer afterwards.
   // K: thread -> (key, 8-wide hd chunk), 16-byte rows. V: thread -> (key pair, 8-wide hd
-  // chunk); the pair is written transposed as 4-byte words vt[d][key, key + 1], lanes of a
-  // wave covering 8 key pairs x 8 hd chunks (bank-conflict free with 17-word rows).
-  constexpr int KCH = KT * HD / 8 / (NW * 64);        // K chunks per thread
-  constexpr int VU = (KT / 2) * (HD / 8);              // V key-pair chunks per tile
-  static_assert(KCH >= 1 && VU <= NW * 64 && KT == 32, "tile / workgroup shape");
-  const bool v_owner = tid < VU;                       // whole waves (VU is 128 or 256)
-  u32x4_t kreg[KCH], vreg[2];
+  // chunk); the pair is written transposed as 4-byte words vt[d][key, key + 1], the 64
+  // lanes of a wave covering 8 key pairs x 8 hd chunks (2-way banked at worst).
+  constexpr int KCH = KT * HD / 8 / (NW * 64);          // K chunks per thread
+  constexpr int VU = (KT / 2) * (HD / 8);                // V key-pair chunks per tile
+  constexpr int VCH = (VU + NW * 64 - 1) / (NW * 64);   // per thread
+  constexpr int KPW = KT / 16;                           // waves along the key pairs
+  static_assert(KCH >= 1 && VU % 64 == 0, "tile / workgroup shape");
+  u32x4_t kreg[KCH], vreg[VCH][2];
+  // Keys past the split's end are clamped to its last key: branch-free loads of finite
+  // data whose scores the mask turns into -inf (P = 0).
   auto key_src = [&](int kk, const uint16_t* cache, const uint16_t* tree, int d0) -> const uint16_t* {
-    return kk < p.C ? cache + ((size_t)kv * p.c_stride + kk) * HD + d0
-                    : tree + ((size_t)kv * p.T + (kk - p.C)) * HD + d0;
+    kk = min(kk, key_end - 1);
+    const uint16_t* a = cache + ((size_t)kv * p.c_stride + kk) * HD + d0;
+    const uint16_t* t = tree + ((size_t)kv * p.T + max(kk - p.C, 0)) * HD + d0;
+    return kk < p.C ? a : t;
+  };
+  auto v_unit = [&](int i, int& kp, int& dc) -> bool {
+    const int u = tid + i * NW * 64;
+    const int w = u >> 6, l = u & 63;
+    kp = (l & 7) + 8 * (w % KPW);
+    dc = (l >> 3) + 8 * (w / KPW);
+    return u < VU;   // whole waves
   };
   auto load_tile = [&](int k0) {
 #pragma unroll
@@ -149,16 +170,17 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnParams p) {
       const int ci = tid + i * NW * 64;
       const int key = ci / (HD / 8), d0 = (ci % (HD / 8)) * 8;
       const int kk = k0 + key;
-      kreg[i] = kk < key_end ? *reinterpret_cast<const u32x4_t*>(key_src(kk, p.kc, p.kt, d0)) : u32x4_t{0u, 0u, 0u, 0u};
+      kreg[i] = *reinterpret_cast<const u32x4_t*>(key_src(kk, p.kc, p.kt, d0));
     }
-    if (v_owner) {
-      const int w = tid >> 6, l = tid & 63;
-      const int kp = (l & 7) + 8 * (w & 1), dc = (l >> 3) + 8 * (w >> 1);
-      const int kk = k0 + 2 * kp;
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        vreg[h] = kk + h < key_end ? *reinterpret_cast<const u32x4_t*>(key_src(kk + h, p.vc, p.vt, dc * 8))
-                                   : u32x4_t{0u, 0u, 0u, 0u};
+    for (int i = 0; i < VCH; ++i) {
+      int kp, dc;
+      if (v_unit(i, kp, dc)) {
+        const int kk = k0 + 2 * kp;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          vreg[i][h] = *reinterpret_cast<const u32x4_t*>(key_src(kk + h, p.vc, p.vt, dc * 8));
+      }
     }
   };
   auto store_tile = [&](int buf) {
@@ -168,18 +190,20 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnParams p) {
       const int key = ci / (HD / 8), d0 = (ci % (HD / 8)) * 8;
       *reinterpret_cast<u32x4_t*>(&k_lds[buf][key * K_STRIDE + d0]) = kreg[i];
     }
-    if (v_owner) {
-      const int w = tid >> 6, l = tid & 63;
-      const int kp = (l & 7) + 8 * (w & 1), dc = (l >> 3) + 8 * (w >> 1);
-      const uint32_t a[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
-      const uint32_t c[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // d = 8 dc + 2e (low halves) and 8 dc + 2e + 1 (high halves) of keys 2kp, 2kp+1
-        uint32_t* row0 = reinterpret_cast<uint32_t*>(&vt_lds[buf][(dc * 8 + 2 * e) * VT_STRIDE]);
-        uint32_t* row1 = reinterpret_cast<uint32_t*>(&vt_lds[buf][(dc * 8 + 2 * e + 1) * VT_STRIDE]);
-        row0[kp] = (a[e] & 0xFFFFu) | (c[e] << 16);
-        row1[kp] = (a[e] >> 16) | (c[e] & 0xFFFF0000u);
+    for (int i = 0; i < VCH; ++i) {
+      int kp, dc;
+      if (v_unit(i, kp, dc)) {
+        const uint32_t a[4] = {vreg[i][0].x, vreg[i][0].y, vreg[i][0].z, vreg[i][0].w};
+        const uint32_t c[4] = {vreg[i][1].x, vreg[i][1].y, vreg[i][1].z, vreg[i][1].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // d = 8 dc + 2e (low halves) and 8 dc + 2e + 1 (high halves) of keys 2kp, 2kp+1
+          uint32_t* row0 = reinterpret_cast<uint32_t*>(&vt_lds[buf][(dc * 8 + 2 * e) * VT_STRIDE]);
+          uint32_t* row1 = reinterpret_cast<uint32_t*>(&vt_lds[buf][(dc * 8 + 2 * e + 1) * VT_STRIDE]);
+          row0[kp] = (a[e] & 0xFFFFu) | (c[e] << 16);
+          row1[kp] = (a[e] >> 16) | (c[e] & 0xFFFF0000u);
+        }
       }
     }
   };
@@ -196,14 +220,14 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnParams p) {
     const uint16_t* kl = k_lds[buf];
     const uint16_t* vl = vt_lds[buf];
 
-    // ---- S^T tiles: keys (rows) x query rows (cols); two 16-key tiles
-    f32x4_t s[QC][2];
+    // ---- S^T tiles: keys (rows) x query rows (cols); 2 NSUB 16-key tiles
+    f32x4_t s[QC][2 * NSUB];
 #pragma unroll
     for (int c = 0; c < QC; ++c)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) s[c][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int kt = 0; kt < 2 * NSUB; ++kt) s[c][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < 2 * NSUB; ++kt) {
 #pragma unroll
       for (int hc = 0; hc < HC; ++hc) {
         const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(&kl[(kt * 16 + j) * K_STRIDE + hc * 32 + b * 8]);
@@ -215,25 +239,34 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnParams p) {
     }
 
     // ---- mask + online softmax. Lane (j, b) holds keys kt*16 + 4b + e of query row j.
-    const bool tree_tile = (k0 + KT > p.C);
+    // tiles wholly inside the prefix and the split need no mask (wave-uniform test)
+    const bool masked = (k0 + KT > p.C) || (k0 + KT > key_end);
 #pragma unroll
     for (int c = 0; c < QC; ++c) {
       float mx = -INFINITY;
+      if (!masked) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2 * NSUB; ++kt)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int kk = k0 + kt * 16 + 4 * b + e;
-          float v = s[c][kt][e] * p.scale_log2;
-          bool vis = kk < key_end;
-          if (vis && tree_tile && kk >= p.C) {
-            const int jn = kk - p.C;
-            vis = (p.mask[(size_t)qtok[c] * W + (jn >> 6)] >> (jn & 63)) & 1ull;
+          for (int e = 0; e < 4; ++e) {
+            const float v = s[c][kt][e] * p.scale_log2;
+            s[c][kt][e] = v;
+            mx = fmaxf(mx, v);
           }
-          v = vis ? v : -INFINITY;
-          s[c][kt][e] = v;
-          mx = fmaxf(mx, v);
-        }
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < 2 * NSUB; ++kt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int kk = k0 + kt * 16 + 4 * b + e;
+            const int jn = kk - p.C;   // tree index (negative in the prefix)
+            const uint64_t mw = jn < 64 ? mw0[c] : jn < 128 ? mw1[c] : jn < 192 ? mw2[c] : mw3[c];
+            const bool vis = kk < key_end && (jn < 0 || ((mw >> (jn & 63)) & 1ull));
+            const float v = vis ? s[c][kt][e] * p.scale_log2 : -INFINITY;
+            s[c][kt][e] = v;
+            mx = fmaxf(mx, v);
+          }
+      }
       mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       // Lazy rescaling: the reference max of a row moves only when the tile's max exceeds
@@ -245,18 +278,20 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnParams p) {
       const float alpha = exp2f(m_run[c] - m_use);   // exp2(-inf) = 0 on the first tile
       const bool any_move = __builtin_amdgcn_ballot_w64(move) != 0;
       float psum = 0.f;
-      uint32_t pk[4];
+      uint32_t pk[NSUB][4];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        float pv[4];
+      for (int sub = 0; sub < NSUB; ++sub)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pv[e] = exp2f(s[c][kt][e] - m_use);
-          psum += pv[e];
+        for (int h = 0; h < 2; ++h) {
+          float pv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pv[e] = exp2f(s[c][2 * sub + h][e] - m_use);
+            psum += pv[e];
+          }
+          pk[sub][h * 2 + 0] = pack_bf16x2(pv[0], pv[1]);
+          pk[sub][h * 2 + 1] = pack_bf16x2(pv[2], pv[3]);
         }
-        pk[kt * 2 + 0] = pack_bf16x2(pv[0], pv[1]);
-        pk[kt * 2 + 1] = pack_bf16x2(pv[2], pv[3]);
-      }
       psum += __shfl_xor(psum, 16, 64);
       psum += __shfl_xor(psum, 32, 64);
       m_run[c] = m_new;
@@ -269,16 +304,20 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnParams p) {
       } else {
         l_run[c] += psum;
       }
-      // P^T operand: lane (j, b) element e' <-> key (e' < 4 ? 4b + e' : 16 + 4b + e' - 4)
-      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[0], pk[1], pk[2], pk[3]});
 #pragma unroll
-      for (int d = 0; d < DT; ++d) {
-        // A operand V^T: lane (i = d row, b) element e' <-> same key permutation
-        const uint32_t* vrow = reinterpret_cast<const uint32_t*>(&vl[(d * 16 + j) * VT_STRIDE]);
-        const u32x2_t lo = {vrow[2 * b], vrow[2 * b + 1]};
-        const u32x2_t hi = {vrow[8 + 2 * b], vrow[8 + 2 * b + 1]};
-        const bf16x8_t va = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
-        o[c][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[c][d], 0, 0, 0);
+      for (int sub = 0; sub < NSUB; ++sub) {
+        // P^T operand of sub-tile sub: lane (j, b) element e' <-> key 32 sub +
+        // (e' < 4 ? 4b + e' : 16 + 4b + e' - 4)
+        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, u32x4_t{pk[sub][0], pk[sub][1], pk[sub][2], pk[sub][3]});
+#pragma unroll
+        for (int d = 0; d < DT; ++d) {
+          // A operand V^T: lane (i = d row, b) element e' <-> the same key permutation
+          const uint32_t* vrow = reinterpret_cast<const uint32_t*>(&vl[(d * 16 + j) * VT_STRIDE + 32 * sub]);
+          const u32x2_t lo = {vrow[2 * b], vrow[2 * b + 1]};
+          const u32x2_t hi = {vrow[8 + 2 * b], vrow[8 + 2 * b + 1]};
+          const bf16x8_t va = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
+          o[c][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[c][d], 0, 0, 0);
+        }
       }
     }
     if (has_next) store_tile(buf ^ 1);   // the other buffer: last read before the previous barrier
@@ -346,10 +385,10 @@ AttnPlan plan_attention(int T, int C, int nq, int nkv, int hd) {
   const int units = pl.qblocks * nkv;
   // aim for ~256 workgroups, keep >= 4 key tiles per split
   int splits = std::max(1, 256 / std::max(1, units));
-  const int max_splits = std::max(1, keys / (4 * KT));
+  const int max_splits = std::max(1, keys / (2 * ATT_KT));
   splits = std::min(splits, max_splits);
   int kps = (keys + splits - 1) / splits;
-  kps = (kps + KT - 1) / KT * KT;
+  kps = (kps + ATT_KT - 1) / ATT_KT * ATT_KT;
   pl.keys_per_split = kps;
   pl.splits = (keys + kps - 1) / kps;
   pl.ws_bytes = (size_t)pl.splits * nkv * rows * (hd + 2) * sizeof(float);
@@ -370,13 +409,13 @@ hipError_t launch_attention(const AttnArgs& a, const AttnPlan& pl, void* ws, hip
   const int qc = attn_qc(p.rows, a.C + a.T);
   dim3 grid(pl.qblocks, a.nkv, pl.splits);
   if (a.hd == 128) {
-    if (qc == 1) hipLaunchKernelGGL((tree_attn_kernel<128, 1>), grid, dim3(256), 0, st, p);
-    else if (qc == 2) hipLaunchKernelGGL((tree_attn_kernel<128, 2>), grid, dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((tree_attn_kernel<128, 3>), grid, dim3(256), 0, st, p);
+    if (qc == 1) hipLaunchKernelGGL((tree_attn_kernel<128, 1, ATT_NSUB>), grid, dim3(256), 0, st, p);
+    else if (qc == 2) hipLaunchKernelGGL((tree_attn_kernel<128, 2, ATT_NSUB>), grid, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((tree_attn_kernel<128, 3, ATT_NSUB>), grid, dim3(256), 0, st, p);
   } else {
-    if (qc == 1) hipLaunchKernelGGL((tree_attn_kernel<64, 1>), grid, dim3(256), 0, st, p);
-    else if (qc == 2) hipLaunchKernelGGL((tree_attn_kernel<64, 2>), grid, dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((tree_attn_kernel<64, 3>), grid, dim3(256), 0, st, p);
+    if (qc == 1) hipLaunchKernelGGL((tree_attn_kernel<64, 1, ATT_NSUB>), grid, dim3(256), 0, st, p);
+    else if (qc == 2) hipLaunchKernelGGL((tree_attn_kernel<64, 2, ATT_NSUB>), grid, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((tree_attn_kernel<64, 3, ATT_NSUB>), grid, dim3(256), 0, st, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
