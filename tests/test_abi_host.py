@@ -1,0 +1,108 @@
+"""The C ABI on the host (no GPU needed): the library loads, exports every function that
+include/subspec.h declares, and rejects bad arguments with the documented status before
+it touches a device.
+
+When the in-tree library has not been built yet, it is built into a temporary folder
+first, so the check never silently passes on a missing library.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from bit_quantized_draft_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "subspec.h")
+
+
+@pytest.fixture(scope="module")
+def L(tmp_path_factory):
+    path = _lib.LIB_PATH
+    if not os.path.exists(path):
+        from bit_quantized_draft_amd import build
+        d = tmp_path_factory.mktemp("lib")
+        path = build.build(verbose=False, out=str(d / "libsubspec.so"), build_dir=str(d / "obj"))
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _lib.SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:ss_status|size_t|int|const char\s*\*)\s*(ss_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("ss_quantize_substitute", "ss_draft_tree_step", "ss_tree_attention", "ss_tree_accept"):
+        assert required in names
+    assert len(names) >= 15, names
+
+
+def test_every_declared_function_is_exported(L):
+    missing = [n for n in declared_functions() if not hasattr(L, n)]
+    assert not missing, f"declared but not exported: {missing}"
+
+
+def test_binding_signatures_cover_the_header():
+    assert set(declared_functions()) == set(_lib.SIGNATURES), (
+        set(declared_functions()) ^ set(_lib.SIGNATURES))
+
+
+def test_version_and_last_error(L):
+    assert L.ss_abi_version() >= 1
+    assert isinstance(L.ss_last_error(), bytes)
+
+
+def _parents(a):
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def test_tree_validate_host(L):
+    a, p = _parents([-1, 0, 1, 1, 0])
+    assert L.ss_tree_validate(p, len(a)) == _lib.SS_OK
+    a, p = _parents([-1] + list(range(63)))   # a chain
+    assert L.ss_tree_validate(p, len(a)) == _lib.SS_OK
+    a, p = _parents([0, 0])                   # root not -1
+    assert L.ss_tree_validate(p, len(a)) == _lib.SS_ERR_BAD_TREE
+    a, p = _parents([-1, 0, 2])               # parent not earlier
+    assert L.ss_tree_validate(p, len(a)) == _lib.SS_ERR_BAD_TREE
+    assert b"parents[2]" in L.ss_last_error()
+    assert L.ss_tree_validate(None, 3) == _lib.SS_ERR_INVALID_ARG
+
+
+def test_linear_argument_checks_before_any_device_call(L):
+    dummy = ctypes.c_void_p(16)   # never dereferenced: validation fails first
+    # T out of range, k not a multiple of 128, n not a multiple of 16, null x
+    assert L.ss_w4a16_linear(dummy, 0, dummy, dummy, dummy, 16, 128, dummy, None, None, 0, None) \
+        == _lib.SS_ERR_UNSUPPORTED
+    assert L.ss_w4a16_linear(dummy, 4, dummy, dummy, dummy, 16, 100, dummy, None, None, 0, None) \
+        == _lib.SS_ERR_UNSUPPORTED
+    assert L.ss_w4a16_linear(dummy, 4, dummy, dummy, dummy, 20, 128, dummy, None, None, 0, None) \
+        == _lib.SS_ERR_UNSUPPORTED
+    assert L.ss_w4a16_linear(None, 4, dummy, dummy, dummy, 16, 128, dummy, None, None, 0, None) \
+        == _lib.SS_ERR_INVALID_ARG
+    assert b"x_bf16" in L.ss_last_error() or b"null" in L.ss_last_error()
+
+
+def test_workspace_queries_are_host_only(L):
+    # sizes follow the work split: 0 when no block is split, else room for the partials
+    assert L.ss_w4a16_linear_workspace(16, 512, 512) >= 0
+    big = L.ss_w4a16_linear_workspace(64, 3584, 18944)   # split blocks: partials needed
+    assert big > 0 and big % 256 == 0
+    assert L.ss_tree_attention_workspace(64, 2048, 28, 4, 128) > 0
+    assert L.ss_tree_attention_workspace(64, 2048, 28, 4, 96) == 0   # unsupported head dim
+
+
+def test_attention_and_step_reject_null_arguments(L):
+    assert L.ss_tree_attention(None, None, 0, None) == _lib.SS_ERR_INVALID_ARG
+    assert L.ss_draft_tree_step(None, None, None, 0, None) == _lib.SS_ERR_INVALID_ARG
