@@ -197,6 +197,8 @@ ss_status check_model(const char* fn, const ss_model* m) {
   if (m->nq / m->nkv > 16) return fail(SS_ERR_UNSUPPORTED, "%s: nq / nkv must be <= 16", fn);
   if (m->H % 128 || m->I % 128 || (m->nq * m->hd) % 128)
     return fail(SS_ERR_UNSUPPORTED, "%s: H, I and nq*hd must be multiples of 128", fn);
+  if (m->H > 8192 || (m->nq + 2 * m->nkv) * m->hd > 8192)
+    return fail(SS_ERR_UNSUPPORTED, "%s: H and (nq + 2 nkv) * hd must be <= 8192", fn);
   if (!m->layers) return fail(SS_ERR_INVALID_ARG, "%s: layers is null", fn);
   if (m->c_stride < 0) return fail(SS_ERR_INVALID_ARG, "%s: c_stride is negative", fn);
   if (!(m->rms_eps >= 0.f) || !(m->rope_theta > 0.f))
@@ -518,15 +520,20 @@ ss_status ss_draft_tree_step(const ss_model* m, const ss_step_args* a, void* wor
     const ss_layer& ly = m->layers[l];
     uint16_t* tk = static_cast<uint16_t*>(a->tree_k[l]);
     uint16_t* tv = static_cast<uint16_t*>(a->tree_v[l]);
-    // attention block
-    RUN(ss::launch_rmsnorm(Ly.h32, static_cast<const uint16_t*>(ly.norm1), T, H, m->rms_eps, Ly.xn, nullptr, T, nullptr, st));
+    // attention block. RMSNorm-1 of layer 0 stands alone; every later RMSNorm is fused
+    // with the residual GEMM before it, which leaves its split blocks to that kernel.
+    if (l == 0)
+      RUN(ss::launch_rmsnorm(Ly.h32, static_cast<const uint16_t*>(ly.norm1), T, H, m->rms_eps, Ly.xn, nullptr, T, nullptr, st));
     {
       ss::GemmArgs g = gemm_args(Ly.xn, T, ly.qkv, qkvN, H);
       g.epi = ss::EPI_STORE;
       g.y_f32 = Ly.qkv32;
-      RUN(ss::launch_gemm(g, ss::plan_gemm(T, qkvN, H, g.epi, 0), Ly.gemm_ws, st));
+      g.defer_reduce = true;
+      const ss::GemmPlan pl = ss::plan_gemm(T, qkvN, H, g.epi, 0);
+      RUN(ss::launch_gemm(g, pl, Ly.gemm_ws, st));
+      RUN(ss::launch_qkv_rope(ss::gemm_split_view(pl, Ly.gemm_ws), Ly.qkv32, Ly.depth, T, C, nq, nkv, hd,
+                              m->rope_theta, Ly.qbuf, tk, tv, st));
     }
-    RUN(ss::launch_rope_split(Ly.qkv32, Ly.depth, T, C, nq, nkv, hd, m->rope_theta, Ly.qbuf, tk, tv, st));
     {
       ss::AttnArgs aa{};
       aa.q = Ly.qbuf;
@@ -541,10 +548,14 @@ ss_status ss_draft_tree_step(const ss_model* m, const ss_step_args* a, void* wor
       ss::GemmArgs g = gemm_args(Ly.attn, T, ly.o, H, nq * hd);
       g.epi = ss::EPI_RESID;
       g.resid = Ly.h32;
-      RUN(ss::launch_gemm(g, ss::plan_gemm(T, H, nq * hd, g.epi, 0), Ly.gemm_ws, st));
+      g.defer_reduce = true;
+      const ss::GemmPlan pl = ss::plan_gemm(T, H, nq * hd, g.epi, 0);
+      RUN(ss::launch_gemm(g, pl, Ly.gemm_ws, st));
+      // residual add of the split blocks + RMSNorm-2
+      RUN(ss::launch_resid_norm(ss::gemm_split_view(pl, Ly.gemm_ws), Ly.h32, T, H,
+                                static_cast<const uint16_t*>(ly.norm2), m->rms_eps, Ly.xn, st));
     }
     // MLP block
-    RUN(ss::launch_rmsnorm(Ly.h32, static_cast<const uint16_t*>(ly.norm2), T, H, m->rms_eps, Ly.xn, nullptr, T, nullptr, st));
     {
       ss::GemmArgs g = gemm_args(Ly.xn, T, ly.gate_up, 2 * I, H);
       g.epi = ss::EPI_SWIGLU;
@@ -556,7 +567,13 @@ ss_status ss_draft_tree_step(const ss_model* m, const ss_step_args* a, void* wor
       ss::GemmArgs g = gemm_args(Ly.ubuf, T, ly.down, H, I);
       g.epi = ss::EPI_RESID;
       g.resid = Ly.h32;
-      RUN(ss::launch_gemm(g, ss::plan_gemm(T, H, I, g.epi, 0), Ly.gemm_ws, st));
+      g.defer_reduce = true;
+      const ss::GemmPlan pl = ss::plan_gemm(T, H, I, g.epi, 0);
+      RUN(ss::launch_gemm(g, pl, Ly.gemm_ws, st));
+      // residual add of the split blocks + the next layer's RMSNorm-1 (none after the last)
+      const uint16_t* next_norm = (l + 1 < m->L) ? static_cast<const uint16_t*>(m->layers[l + 1].norm1) : nullptr;
+      RUN(ss::launch_resid_norm(ss::gemm_split_view(pl, Ly.gemm_ws), Ly.h32, T, H, next_norm, m->rms_eps,
+                                Ly.xn, st));
     }
   }
   if (a->hidden_out) RUN(ss::launch_f32_to_bf16(Ly.h32, (size_t)T * H, static_cast<uint16_t*>(a->hidden_out), st));

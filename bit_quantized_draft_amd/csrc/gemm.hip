@@ -688,7 +688,7 @@ constexpr int kPF = SS_GEMM_PF;     // int4 weight steps in flight per wave
 constexpr int kPFB = SS_GEMM_PFB;   // bf16 weight steps in flight per wave
 
 template <int TT, bool INT4, int EPI, int KS>
-hipError_t launch_k(const GemmParams& p, int sk_blocks, hipStream_t st) {
+hipError_t launch_k(const GemmParams& p, int sk_blocks, bool defer, hipStream_t st) {
   constexpr int PF = INT4 ? kPF : kPFB;
   constexpr bool CAN_SZO = INT4 && KS == 1;
   const bool aligned16 = (reinterpret_cast<uintptr_t>(p.sc) % 16 == 0) && (reinterpret_cast<uintptr_t>(p.zp) % 16 == 0);
@@ -697,26 +697,26 @@ hipError_t launch_k(const GemmParams& p, int sk_blocks, hipStream_t st) {
   else
     hipLaunchKernelGGL((w4_gemm_kernel<TT, INT4, EPI, KS, PF, false>), dim3(p.G), dim3((NWC + NLD) * 64), 0, st, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || sk_blocks == 0) return e;
+  if (e != hipSuccess || sk_blocks == 0 || defer) return e;
   constexpr int per_block = (NWC / KS) * (EPI == EPI_SWIGLU ? 1 : NR) * TT * 4 * 64;
   hipLaunchKernelGGL((sk_reduce_kernel<TT, EPI, KS>), dim3(sk_blocks, (per_block + 255) / 256), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
 template <bool INT4, int EPI, int KS>
-hipError_t launch_tt(const GemmParams& p, int TT, int skb, hipStream_t st) {
+hipError_t launch_tt(const GemmParams& p, int TT, int skb, bool defer, hipStream_t st) {
   switch (TT) {
-    case 1: return launch_k<1, INT4, EPI, KS>(p, skb, st);
-    case 2: return launch_k<2, INT4, EPI, KS>(p, skb, st);
-    case 3: return launch_k<3, INT4, EPI, KS>(p, skb, st);
-    default: return launch_k<4, INT4, EPI, KS>(p, skb, st);
+    case 1: return launch_k<1, INT4, EPI, KS>(p, skb, defer, st);
+    case 2: return launch_k<2, INT4, EPI, KS>(p, skb, defer, st);
+    case 3: return launch_k<3, INT4, EPI, KS>(p, skb, defer, st);
+    default: return launch_k<4, INT4, EPI, KS>(p, skb, defer, st);
   }
 }
 
 template <int EPI>
-hipError_t launch_epi(const GemmParams& p, bool int4, int TT, int KS, int skb, hipStream_t st) {
-  if (KS == 1) return int4 ? launch_tt<true, EPI, 1>(p, TT, skb, st) : launch_tt<false, EPI, 1>(p, TT, skb, st);
-  return int4 ? launch_tt<true, EPI, 2>(p, TT, skb, st) : launch_tt<false, EPI, 2>(p, TT, skb, st);
+hipError_t launch_epi(const GemmParams& p, bool int4, int TT, int KS, int skb, bool defer, hipStream_t st) {
+  if (KS == 1) return int4 ? launch_tt<true, EPI, 1>(p, TT, skb, defer, st) : launch_tt<false, EPI, 1>(p, TT, skb, defer, st);
+  return int4 ? launch_tt<true, EPI, 2>(p, TT, skb, defer, st) : launch_tt<false, EPI, 2>(p, TT, skb, defer, st);
 }
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
@@ -763,11 +763,27 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& pl, void* ws, hipStrea
   p.sk_units = pl.sk_units;
   p.partials = pl.sk_blocks > 0 ? reinterpret_cast<float*>(ws) : nullptr;
   const bool int4 = a.qw != nullptr;
+  const bool defer = a.defer_reduce && a.epi != EPI_SWIGLU;
   switch (a.epi) {
-    case EPI_RESID: return launch_epi<EPI_RESID>(p, int4, pl.TT, pl.KS, pl.sk_blocks, st);
-    case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(p, int4, pl.TT, pl.KS, pl.sk_blocks, st);
-    default: return launch_epi<EPI_STORE>(p, int4, pl.TT, pl.KS, pl.sk_blocks, st);
+    case EPI_RESID: return launch_epi<EPI_RESID>(p, int4, pl.TT, pl.KS, pl.sk_blocks, defer, st);
+    case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(p, int4, pl.TT, pl.KS, pl.sk_blocks, false, st);
+    default: return launch_epi<EPI_STORE>(p, int4, pl.TT, pl.KS, pl.sk_blocks, defer, st);
   }
+}
+
+SplitView gemm_split_view(const GemmPlan& pl, const void* ws) {
+  SplitView v{};
+  v.partials = pl.sk_blocks > 0 ? static_cast<const float*>(ws) : nullptr;
+  v.RG = NWC / pl.KS;
+  v.TT = pl.TT;
+  v.tb_count = pl.tb_count;
+  v.rows_per_block = v.RG * 32;
+  v.rb_count = pl.rb_count;
+  v.nsteps = pl.nsteps;
+  v.G_sk = pl.G_sk;
+  v.sk_first = pl.sk_first;
+  v.sk_units = pl.sk_units;
+  return v;
 }
 
 }  // namespace ss

@@ -24,6 +24,7 @@ struct GemmArgs {
   uint16_t* y_bf16;
   float* resid;
   uint16_t* u_bf16;
+  bool defer_reduce;   // leave split blocks' partials for the consumer (see SplitView)
 };
 
 // Decomposition of one GEMM call: row blocks x token blocks, each cut into steps of KS
@@ -39,6 +40,26 @@ struct GemmPlan {
 
 GemmPlan plan_gemm(int T, int N, int K, int epi, int swiglu_I);
 hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& pl, void* ws, hipStream_t st);
+
+// Where a GEMM launched with defer_reduce left its split blocks' partials (device-side
+// accessors in split_view.h). Non-SwiGLU epilogues only.
+struct SplitView {
+  const float* partials;
+  int RG, TT, tb_count, rows_per_block, rb_count, nsteps, G_sk, sk_first;
+  long long sk_units;
+};
+SplitView gemm_split_view(const GemmPlan& pl, const void* ws);
+
+// Finish a deferred residual GEMM and normalize: for every token row t, h32[t] += the
+// split blocks' sums, then xn[t] = bf16(h32[t] * rsqrt(mean(h32[t]^2) + eps) * gain) when
+// gain is not null. H <= 8192.
+hipError_t launch_resid_norm(const SplitView& v, float* h32, int T, int H, const uint16_t* gain,
+                             float eps, uint16_t* xn, hipStream_t st);
+// Finish a deferred qkv GEMM (values of unsplit blocks are read from qkv32) and apply
+// RoPE + the q / tree-K / tree-V scatter of launch_rope_split.
+hipError_t launch_qkv_rope(const SplitView& v, const float* qkv32, const int32_t* depth, int T, int C,
+                           int nq, int nkv, int hd, float theta, uint16_t* q, uint16_t* kt,
+                           uint16_t* vt, hipStream_t st);
 
 // quantization
 hipError_t launch_quantize_g64(const uint16_t* w, int64_t n, int64_t k, uint8_t* q, uint16_t* s,

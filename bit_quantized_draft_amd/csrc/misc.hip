@@ -9,6 +9,7 @@
 // (Review §6.3); read as Gumbel-top-k sampling without replacement.
 #include "common.h"
 #include "kernels.h"
+#include "split_view.h"
 
 namespace ss {
 
@@ -127,6 +128,136 @@ __global__ __launch_bounds__(256) void rope_split_kernel(const float* __restrict
     const int kh = i / hd, d = i % hd;
     vt[((size_t)kh * T + t) * hd + d] = f32_to_bf16(row[(nq + nkv) * hd + i]);
   }
+}
+
+// ------------------------------------------------------------------ fused split finish
+
+constexpr int SV_THREADS = 1024;
+constexpr int SV_MAX_BLOCKS = 128;   // row blocks per token row
+constexpr int SV_MAX_W = 8192;       // row width (SV_THREADS * the largest KM)
+
+// One workgroup per token row: finish the split blocks of a residual GEMM into h32[t]
+// (h += sum of pieces; blocks the GEMM stored itself are already in h32), then, when gain
+// is given, the row's RMSNorm into xn.
+template <int KM>
+__global__ __launch_bounds__(SV_THREADS) void resid_norm_kernel(SplitView v, float* __restrict__ h32, int H,
+                                                                const uint16_t* __restrict__ gain, float eps,
+                                                                uint16_t* __restrict__ xn) {
+  __shared__ SvBlock blk[SV_MAX_BLOCKS];
+  __shared__ float red[SV_THREADS / 64];
+  const int t = blockIdx.x, tb = t >> 6;
+  for (int rb = threadIdx.x; rb < v.rb_count; rb += blockDim.x) blk[rb] = sv_block(v, tb + rb * v.tb_count);
+  __syncthreads();
+  float* row = h32 + (size_t)t * H;
+  float hv[KM];
+  sv_row<KM>(v, blk, t, H, row, true, hv);
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < KM; ++k) {
+    const int n = k * SV_THREADS + threadIdx.x;
+    if (n < H) {
+      const SvBlock b = blk[n / v.rows_per_block];
+      if (b.g1 != b.g0) row[n] = hv[k];
+      ss += hv[k] * hv[k];
+    }
+  }
+  if (!gain) return;
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < SV_THREADS / 64; ++w) tot += red[w];
+  const float rs = 1.0f / sqrtf(tot / (float)H + eps);
+  uint16_t* o = xn + (size_t)t * H;
+#pragma unroll
+  for (int k = 0; k < KM; ++k) {
+    const int n = k * SV_THREADS + threadIdx.x;
+    if (n < H) o[n] = f32_to_bf16(hv[k] * rs * bf16_to_f32(gain[n]));
+  }
+}
+
+// One workgroup per token row: finish the split qkv blocks into LDS, then RoPE
+// (rotate-half) on q and k at position C + depth[t] with fp64 angles, and scatter to q
+// [T][nq][hd] and tree K / V [nkv][T][hd] (bf16).
+template <int KM>
+__global__ __launch_bounds__(SV_THREADS) void qkv_rope_kernel(SplitView v, const float* __restrict__ qkv,
+                                                              const int32_t* __restrict__ depth, int T, int C,
+                                                              int nq, int nkv, int hd, double theta,
+                                                              uint16_t* __restrict__ q, uint16_t* __restrict__ kt,
+                                                              uint16_t* __restrict__ vt) {
+  __shared__ SvBlock blk[SV_MAX_BLOCKS];
+  __shared__ float rowv[SV_MAX_W];
+  __shared__ float cs[64], sn[64];   // hd <= 128
+  const int t = blockIdx.x, tb = t >> 6;
+  const int half = hd >> 1;
+  const int W = (nq + 2 * nkv) * hd;
+  for (int rb = threadIdx.x; rb < v.rb_count; rb += blockDim.x) blk[rb] = sv_block(v, tb + rb * v.tb_count);
+  if (threadIdx.x < half) {
+    const double pos = (double)(C + depth[t]);
+    const double inv = pow(theta, -2.0 * (double)threadIdx.x / (double)hd);
+    double sd, cd;
+    sincos(pos * inv, &sd, &cd);
+    cs[threadIdx.x] = (float)cd;
+    sn[threadIdx.x] = (float)sd;
+  }
+  __syncthreads();
+  float val[KM];
+  sv_row<KM>(v, blk, t, W, qkv + (size_t)t * W, false, val);
+#pragma unroll
+  for (int k = 0; k < KM; ++k) {
+    const int n = k * SV_THREADS + threadIdx.x;
+    if (n < W) rowv[n] = val[k];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < (nq + nkv) * half; e += blockDim.x) {
+    const int h = e / half, i = e - h * half;
+    const float c = cs[i], s = sn[i];
+    const float a = rowv[h * hd + i], bb = rowv[h * hd + i + half];
+    const float r0 = a * c - bb * s;
+    const float r1 = bb * c + a * s;
+    uint16_t* dst = (h < nq) ? q + ((size_t)t * nq + h) * hd : kt + ((size_t)(h - nq) * T + t) * hd;
+    dst[i] = f32_to_bf16(r0);
+    dst[i + half] = f32_to_bf16(r1);
+  }
+  for (int i = threadIdx.x; i < nkv * hd; i += blockDim.x) {
+    const int kh = i / hd, d = i % hd;
+    vt[((size_t)kh * T + t) * hd + d] = f32_to_bf16(rowv[(nq + nkv) * hd + i]);
+  }
+}
+
+namespace {
+int sv_km(int W) {
+  const int need = (W + SV_THREADS - 1) / SV_THREADS;
+  return need <= 2 ? 2 : need <= 4 ? 4 : need <= 6 ? 6 : 8;
+}
+}  // namespace
+
+hipError_t launch_resid_norm(const SplitView& v, float* h32, int T, int H, const uint16_t* gain,
+                             float eps, uint16_t* xn, hipStream_t st) {
+  if (H > SV_MAX_W || v.rb_count > SV_MAX_BLOCKS) return hipErrorInvalidValue;
+  switch (sv_km(H)) {
+    case 2: hipLaunchKernelGGL(resid_norm_kernel<2>, dim3(T), dim3(SV_THREADS), 0, st, v, h32, H, gain, eps, xn); break;
+    case 4: hipLaunchKernelGGL(resid_norm_kernel<4>, dim3(T), dim3(SV_THREADS), 0, st, v, h32, H, gain, eps, xn); break;
+    case 6: hipLaunchKernelGGL(resid_norm_kernel<6>, dim3(T), dim3(SV_THREADS), 0, st, v, h32, H, gain, eps, xn); break;
+    default: hipLaunchKernelGGL(resid_norm_kernel<8>, dim3(T), dim3(SV_THREADS), 0, st, v, h32, H, gain, eps, xn); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_qkv_rope(const SplitView& v, const float* qkv32, const int32_t* depth, int T, int C,
+                           int nq, int nkv, int hd, float theta, uint16_t* q, uint16_t* kt,
+                           uint16_t* vt, hipStream_t st) {
+  const int W = (nq + 2 * nkv) * hd;
+  if (W > SV_MAX_W || v.rb_count > SV_MAX_BLOCKS || hd > 128) return hipErrorInvalidValue;
+  const double th = theta;
+  switch (sv_km(W)) {
+    case 2: hipLaunchKernelGGL(qkv_rope_kernel<2>, dim3(T), dim3(SV_THREADS), 0, st, v, qkv32, depth, T, C, nq, nkv, hd, th, q, kt, vt); break;
+    case 4: hipLaunchKernelGGL(qkv_rope_kernel<4>, dim3(T), dim3(SV_THREADS), 0, st, v, qkv32, depth, T, C, nq, nkv, hd, th, q, kt, vt); break;
+    case 6: hipLaunchKernelGGL(qkv_rope_kernel<6>, dim3(T), dim3(SV_THREADS), 0, st, v, qkv32, depth, T, C, nq, nkv, hd, th, q, kt, vt); break;
+    default: hipLaunchKernelGGL(qkv_rope_kernel<8>, dim3(T), dim3(SV_THREADS), 0, st, v, qkv32, depth, T, C, nq, nkv, hd, th, q, kt, vt); break;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_embed(const int32_t* tokens, const uint16_t* embed, int T, int H, int V, float* h32,
@@ -256,23 +387,26 @@ __global__ __launch_bounds__(SCAN_THREADS) void row_argmax_kernel(const float* _
 
 constexpr int SEL_MAX = 16;
 
+// KM: length of each thread's sorted candidate list (>= k); the kernel is instantiated
+// for a few list lengths so the common k = 6 does not pay for 16-entry insertions.
+template <int KM>
 __global__ __launch_bounds__(SCAN_THREADS) void draft_select_kernel(const float* __restrict__ logits,
                                                                     const float* __restrict__ gumbel,
                                                                     int vocab, float inv_temp, int k,
                                                                     int32_t* __restrict__ out) {
   const size_t off = (size_t)blockIdx.x * vocab;
-  float tv[SEL_MAX];
-  int ti[SEL_MAX];
+  float tv[KM];
+  int ti[KM];
 #pragma unroll
-  for (int s = 0; s < SEL_MAX; ++s) { tv[s] = -INFINITY; ti[s] = 0x7FFFFFFF; }
+  for (int s = 0; s < KM; ++s) { tv[s] = -INFINITY; ti[s] = 0x7FFFFFFF; }
   // y = fp32(fp32(logit * inv_temp) + g): two roundings (the library is built without
   // contraction); with no noise, y + 0 is y
   scan_row(logits + off, gumbel ? gumbel + off : nullptr, vocab, inv_temp, [&](float y, int i) {
-    if (!better(y, i, tv[SEL_MAX - 1], ti[SEL_MAX - 1])) return;
+    if (!better(y, i, tv[KM - 1], ti[KM - 1])) return;
     float cv = y;
     int ci = i;
 #pragma unroll
-    for (int s = 0; s < SEL_MAX; ++s) {
+    for (int s = 0; s < KM; ++s) {
       if (better(cv, ci, tv[s], ti[s])) {
         const float xv = tv[s];
         const int xi = ti[s];
@@ -286,9 +420,9 @@ __global__ __launch_bounds__(SCAN_THREADS) void draft_select_kernel(const float*
     if (threadIdx.x == 0) out[(size_t)blockIdx.x * k + r] = w.i;
     if (ti[0] == w.i) {   // the owner pops its head
 #pragma unroll
-      for (int s = 0; s < SEL_MAX - 1; ++s) { tv[s] = tv[s + 1]; ti[s] = ti[s + 1]; }
-      tv[SEL_MAX - 1] = -INFINITY;
-      ti[SEL_MAX - 1] = 0x7FFFFFFF;
+      for (int s = 0; s < KM - 1; ++s) { tv[s] = tv[s + 1]; ti[s] = ti[s + 1]; }
+      tv[KM - 1] = -INFINITY;
+      ti[KM - 1] = 0x7FFFFFFF;
     }
   }
 }
@@ -299,8 +433,12 @@ hipError_t launch_row_argmax(const float* logits, int rows, int vocab, int32_t* 
 }
 hipError_t launch_draft_select(const float* logits, const float* gumbel, int rows, int vocab,
                                float inv_temp, int k, int32_t* out, hipStream_t st) {
-  hipLaunchKernelGGL(draft_select_kernel, dim3(rows), dim3(SCAN_THREADS), 0, st, logits, gumbel, vocab,
-                     inv_temp, k, out);
+  if (k <= 2)
+    hipLaunchKernelGGL(draft_select_kernel<2>, dim3(rows), dim3(SCAN_THREADS), 0, st, logits, gumbel, vocab, inv_temp, k, out);
+  else if (k <= 6)
+    hipLaunchKernelGGL(draft_select_kernel<6>, dim3(rows), dim3(SCAN_THREADS), 0, st, logits, gumbel, vocab, inv_temp, k, out);
+  else
+    hipLaunchKernelGGL(draft_select_kernel<SEL_MAX>, dim3(rows), dim3(SCAN_THREADS), 0, st, logits, gumbel, vocab, inv_temp, k, out);
   return hipGetLastError();
 }
 

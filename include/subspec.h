@@ -199,7 +199,8 @@ typedef struct {
   int32_t n_logit_rows;     /* R when logit_rows is given */
 } ss_step_args;
 
-/* 1 <= T <= 256; H, nq hd, I multiples of 128; hd in {64, 128}; nq % nkv == 0. */
+/* 1 <= T <= 256; H, nq hd, I multiples of 128; H <= 8192 and (nq + 2 nkv) hd <= 8192;
+ * hd in {64, 128}; nq % nkv == 0 (else SS_ERR_UNSUPPORTED). */
 size_t ss_draft_tree_step_workspace(const ss_model* model, int32_t T, int32_t C);
 ss_status ss_draft_tree_step(const ss_model* model, const ss_step_args* args, void* workspace,
                              size_t ws_bytes, void* stream);
