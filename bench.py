@@ -43,6 +43,12 @@ def parse():
     ap.add_argument("--layers", type=int, default=None, help="override the layer count (debug only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--pmc-probe", action="store_true",
+                    help="run only the dominant kernel over rotated weights, then a 256 MiB "
+                         "negation as the counter calibration (for rocprofv3 --pmc passes)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) of "
+                         "--pmc-probe into the traffic summary under profiles/ (CPU only)")
     return ap.parse_args()
 
 
@@ -150,9 +156,121 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
+PMC_JSON = os.path.join(ROOT, "profiles", "gate_up_swiglu_qwen7b_T64_pmc.json")
+PMC_MD = os.path.join(ROOT, "profiles", "gate_up_swiglu_qwen7b_T64_pmc.md")
+CAL_BYTES = 256 << 20          # calibration: fp32 negation reads and writes this many bytes
+
+
+def gate_up_bytes(cfg):
+    """Algorithmic bytes of one gate_up launch: int4 codes + fp16 scale/zero (0.5625 B per
+    weight), bf16 activations in, bf16 SwiGLU output."""
+    return 0.5625 * 2 * cfg.I * cfg.H + cfg.T * cfg.H * 2 + cfg.T * cfg.I * 2
+
+
+def pmc_probe(args):
+    """The dominant kernel alone: gate_up + SwiGLU (int4, T=64) over 8 weight copies in
+    rotation (more than the 256 MB Infinity Cache), then the calibration negation."""
+    import torch
+    import bit_quantized_draft_amd as bq
+    from synth import gen
+    from synth.configs import get_config
+    cfg = get_config(3)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    rot = []
+    for li in range(8):
+        w = gen.torch_normal_bf16((2 * cfg.I, cfg.H), cfg.w_std, 0, cfg.cid, gen.TID_W,
+                                  li * 16 + gen.SLOT["gate_up"], dev)
+        rot.append(bq.quantize_substitute(w))
+        del w
+    x = gen.torch_normal_bf16((cfg.T, cfg.H), 1.0, 0, cfg.cid, gen.TID_X, 0, dev)
+    u = torch.empty((cfg.T, cfg.I), dtype=torch.bfloat16, device=dev)
+    a = torch.ones(CAL_BYTES // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for r in range(args.kernel_reps):
+        for q, sc, z in rot:
+            bq.w4a16_gate_up_swiglu(x, q, sc, z, out=u)
+    torch.cuda.synchronize()
+    torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    print(f"pmc probe done: {8 * args.kernel_reps} gate_up launches, one {CAL_BYTES >> 20} MiB negation",
+          flush=True)
+
+
+def _counter_rows(folder, counter):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {folder}")
+    per = {}
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (r.get("Dispatch_Id") or r.get("Correlation_Id"), r["Kernel_Name"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    return per
+
+
+def pmc_summary(fetch_dir, write_dir):
+    from synth.configs import get_config
+    cfg = get_config(3)
+    out = {}
+    for counter, folder in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(folder, counter)
+        gemm = [v for (_, k), v in rows.items() if "w4_gemm_kernel" in k]
+        red = [v for (_, k), v in rows.items() if "sk_reduce_kernel" in k]
+        cal = [v for (_, k), v in rows.items() if "neg" in k.lower()]
+        if not gemm or len(cal) != 1:
+            raise SystemExit(f"{counter}: expected gate_up dispatches and one calibration dispatch, "
+                             f"found {len(gemm)} and {len(cal)}")
+        factor = CAL_BYTES / (cal[0] * 1024.0)
+        g = sum(gemm) / len(gemm) * 1024.0 * factor
+        r = (sum(red) / len(red) * 1024.0 * factor) if red else 0.0
+        out[counter] = {"kib_per_dispatch_gemm": sum(gemm) / len(gemm),
+                        "kib_per_dispatch_reduce": (sum(red) / len(red)) if red else 0.0,
+                        "kib_calibration": cal[0], "scale_factor": factor,
+                        "bytes_gemm": g, "bytes_reduce": r, "dispatches": len(gemm)}
+    alg = gate_up_bytes(cfg)
+    hbm = sum(v["bytes_gemm"] + v["bytes_reduce"] for v in out.values())
+    d = {"kernel": "w4_gemm_kernel<T=64, int4, EPI_SWIGLU> + sk_reduce_kernel (gate_up 37888x3584, T=64)",
+         "source_hash": kernel_source_hash(), "alg_bytes_per_launch": int(alg),
+         "hbm_bytes_per_launch": int(hbm), "hbm_over_alg": round(hbm / alg, 4), "counters": out}
+    with open(PMC_JSON, "w") as fh:
+        json.dump(d, fh, indent=1)
+    lines = [
+        "# gate_up + SwiGLU (int4 g64, 37888 x 3584, T=64): HBM traffic from PMC counters",
+        "",
+        "Commands (from the repository root on the GPU host; each pass its own run):",
+        "",
+        "```",
+        "cd /tmp && timeout -s KILL 90 rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out>/fetch -o run -- python3 <repo>/bench.py --pmc-probe --kernel-reps 2",
+        "cd /tmp && timeout -s KILL 90 rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out>/write -o run -- python3 <repo>/bench.py --pmc-probe --kernel-reps 2",
+        "python3 bench.py --pmc-summary <out>/fetch <out>/write",
+        "```",
+        "",
+        f"Kernel sources hash (gemm.hip, common.h, kernels.h): `{d['source_hash']}`",
+        "",
+        "| counter | KiB/dispatch GEMM | KiB/dispatch reduce | KiB calibration (256 MiB) | factor | bytes/launch |",
+        "|---|---|---|---|---|---|",
+    ]
+    for c, v in out.items():
+        lines.append(f"| {c} | {v['kib_per_dispatch_gemm']:.1f} | {v['kib_per_dispatch_reduce']:.1f} | "
+                     f"{v['kib_calibration']:.1f} | {v['scale_factor']:.3f} | "
+                     f"{v['bytes_gemm'] + v['bytes_reduce']:.0f} |")
+    lines += ["", f"Algorithmic bytes per launch: {int(alg)}; measured HBM bytes per launch: {int(hbm)} "
+              f"({hbm / alg:.3f} x algorithmic).", ""]
+    with open(PMC_MD, "w") as fh:
+        fh.write("\n".join(lines))
+    print(json.dumps(d))
+
+
 def traffic_from_profile(bytes_alg):
     """HBM bytes per launch of the dominant kernel from committed PMC summaries, or None."""
-    path = os.path.join(ROOT, "profiles", "gate_up_swiglu_qwen7b_T64_pmc.json")
+    path = PMC_JSON
     if not os.path.exists(path):
         return None
     with open(path) as fh:
@@ -166,10 +284,16 @@ def traffic_from_profile(bytes_alg):
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
               f"(--gpus {args.gpus} requested).", file=sys.stderr)
         sys.exit(2)
+    if args.pmc_probe:
+        pmc_probe(args)
+        return
     import torch
     import bit_quantized_draft_amd as bq
     from synth import gen
@@ -288,7 +412,7 @@ def main():
         k1.record(ks)
     torch.cuda.synchronize()
     us_launch = k0.elapsed_time(k1) * 1e3 / n_launch
-    gu_bytes = 0.5625 * 2 * cfg.I * cfg.H + T * cfg.H * 2 + T * cfg.I * 2
+    gu_bytes = gate_up_bytes(cfg)
     achieved = gu_bytes / (us_launch * 1e-6) / 1e9
 
     cpu = None

@@ -132,9 +132,13 @@ __global__ __launch_bounds__(256) void rope_split_kernel(const float* __restrict
 
 // ------------------------------------------------------------------ fused split finish
 
-constexpr int SV_THREADS = 1024;
+#ifndef SS_SV_THREADS
+#define SS_SV_THREADS 1024
+#endif
+constexpr int SV_THREADS = SS_SV_THREADS;
 constexpr int SV_MAX_BLOCKS = 128;   // row blocks per token row
-constexpr int SV_MAX_W = 8192;       // row width (SV_THREADS * the largest KM)
+constexpr int SV_MAX_W = 8192;       // row width
+static_assert(SV_THREADS * 8 >= SV_MAX_W, "the largest KM (8) must cover a row");
 
 // One workgroup per token row: finish the split blocks of a residual GEMM into h32[t]
 // (h += sum of pieces; blocks the GEMM stored itself are already in h32), then, when gain
@@ -231,11 +235,15 @@ int sv_km(int W) {
   const int need = (W + SV_THREADS - 1) / SV_THREADS;
   return need <= 2 ? 2 : need <= 4 ? 4 : need <= 6 ? 6 : 8;
 }
+// the kernels' 32-bit ownership arithmetic and their per-thread element count
+bool sv_fits(const SplitView& v) {
+  return v.sk_units * (long long)std::max(v.G_sk, 1) < (1LL << 31) && v.nsteps > 0;
+}
 }  // namespace
 
 hipError_t launch_resid_norm(const SplitView& v, float* h32, int T, int H, const uint16_t* gain,
                              float eps, uint16_t* xn, hipStream_t st) {
-  if (H > SV_MAX_W || v.rb_count > SV_MAX_BLOCKS) return hipErrorInvalidValue;
+  if (H > SV_MAX_W || v.rb_count > SV_MAX_BLOCKS || !sv_fits(v)) return hipErrorInvalidValue;
   switch (sv_km(H)) {
     case 2: hipLaunchKernelGGL(resid_norm_kernel<2>, dim3(T), dim3(SV_THREADS), 0, st, v, h32, H, gain, eps, xn); break;
     case 4: hipLaunchKernelGGL(resid_norm_kernel<4>, dim3(T), dim3(SV_THREADS), 0, st, v, h32, H, gain, eps, xn); break;
@@ -249,7 +257,7 @@ hipError_t launch_qkv_rope(const SplitView& v, const float* qkv32, const int32_t
                            int nq, int nkv, int hd, float theta, uint16_t* q, uint16_t* kt,
                            uint16_t* vt, hipStream_t st) {
   const int W = (nq + 2 * nkv) * hd;
-  if (W > SV_MAX_W || v.rb_count > SV_MAX_BLOCKS || hd > 128) return hipErrorInvalidValue;
+  if (W > SV_MAX_W || v.rb_count > SV_MAX_BLOCKS || hd > 128 || !sv_fits(v)) return hipErrorInvalidValue;
   const double th = theta;
   switch (sv_km(W)) {
     case 2: hipLaunchKernelGGL(qkv_rope_kernel<2>, dim3(T), dim3(SV_THREADS), 0, st, v, qkv32, depth, T, C, nq, nkv, hd, th, q, kt, vt); break;

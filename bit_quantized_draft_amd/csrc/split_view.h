@@ -15,19 +15,20 @@ struct SvBlock {
   int slot0;     // partial slot of the first piece (the others use slot 2 gk)
 };
 
-__device__ __forceinline__ int sv_owner(const SplitView& v, long long u) {
-  return (int)(((u + 1) * v.G_sk - 1) / v.sk_units);
+// Ownership arithmetic in 32 bits: the launchers check sk_units * G_sk < 2^31.
+__device__ __forceinline__ int sv_owner(const SplitView& v, uint32_t u) {
+  return (int)(((u + 1) * (uint32_t)v.G_sk - 1) / (uint32_t)v.sk_units);
 }
 
 __device__ __forceinline__ SvBlock sv_block(const SplitView& v, int b) {
   SvBlock r{0, 0, 0};
   if (b < v.sk_first) return r;
   const int sb = b - v.sk_first;
-  const long long u0 = (long long)sb * v.nsteps;
+  const uint32_t u0 = (uint32_t)sb * (uint32_t)v.nsteps;
   r.g0 = sv_owner(v, u0);
   r.g1 = sv_owner(v, u0 + v.nsteps - 1);
-  const long long lo = (long long)r.g0 * v.sk_units / v.G_sk;
-  r.slot0 = 2 * r.g0 + ((int)(lo / v.nsteps) == sb ? 0 : 1);
+  const uint32_t lo = (uint32_t)r.g0 * (uint32_t)v.sk_units / (uint32_t)v.G_sk;
+  r.slot0 = 2 * r.g0 + ((int)(lo / (uint32_t)v.nsteps) == sb ? 0 : 1);
   return r;
 }
 
@@ -45,7 +46,10 @@ __device__ __forceinline__ size_t sv_offset(const SplitView& v, int t, int n) {
 // the sum of its pieces in K order from 0, plus row[n] when add_row (a residual); any
 // other element is row[n] as the GEMM left it. Piece loads go out SV_BATCH at a time per
 // element, all independent, and are added afterwards in order.
-constexpr int SV_BATCH = 8;
+#ifndef SS_SV_BATCH
+#define SS_SV_BATCH 8
+#endif
+constexpr int SV_BATCH = SS_SV_BATCH;
 
 template <int KM>
 __device__ __forceinline__ void sv_row(const SplitView& v, const SvBlock* blk, int t, int W,
