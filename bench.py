@@ -70,7 +70,7 @@ def build_model(cfg, dev, n_layers):
         d, t = {}, {}
         for name, N, K in layer_shapes(cfg):
             w = gen.torch_normal_bf16((N, K), cfg.w_std, 0, cfg.cid, gen.TID_W, li * 16 + gen.SLOT[name], dev)
-            d[name] = bq.quantize_substitute(w)
+            d[name] = bq.w4_tile(*bq.quantize_substitute(w))   # the tiled layout the GEMMs stream
             t[name] = w
         kc = gen.torch_normal_bf16((cfg.nkv, cfg.C, cfg.hd), 1.0, 0, cfg.cid, gen.TID_KC, li, dev)
         vc = gen.torch_normal_bf16((cfg.nkv, cfg.C, cfg.hd), 1.0, 0, cfg.cid, gen.TID_VC, li, dev)
@@ -168,7 +168,7 @@ def gate_up_bytes(cfg):
 
 
 def pmc_probe(args):
-    """The dominant kernel alone: gate_up + SwiGLU (int4, T=64) over 8 weight copies in
+    """The dominant kernel alone: tiled gate_up + SwiGLU (int4, T=64) over 8 weight copies in
     rotation (more than the 256 MB Infinity Cache), then the calibration negation."""
     import torch
     import bit_quantized_draft_amd as bq
@@ -181,7 +181,7 @@ def pmc_probe(args):
     for li in range(8):
         w = gen.torch_normal_bf16((2 * cfg.I, cfg.H), cfg.w_std, 0, cfg.cid, gen.TID_W,
                                   li * 16 + gen.SLOT["gate_up"], dev)
-        rot.append(bq.quantize_substitute(w))
+        rot.append(bq.w4_tile(*bq.quantize_substitute(w)))
         del w
     x = gen.torch_normal_bf16((cfg.T, cfg.H), 1.0, 0, cfg.cid, gen.TID_X, 0, dev)
     u = torch.empty((cfg.T, cfg.I), dtype=torch.bfloat16, device=dev)
@@ -189,8 +189,8 @@ def pmc_probe(args):
     b = torch.empty_like(a)
     torch.cuda.synchronize()
     for r in range(args.kernel_reps):
-        for q, sc, z in rot:
-            bq.w4a16_gate_up_swiglu(x, q, sc, z, out=u)
+        for tw in rot:
+            bq.w4a16_gate_up_swiglu_tiled(x, tw, out=u)
     torch.cuda.synchronize()
     torch.neg(a, out=b)
     torch.cuda.synchronize()
@@ -221,7 +221,7 @@ def pmc_summary(fetch_dir, write_dir):
     out = {}
     for counter, folder in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _counter_rows(folder, counter)
-        gemm = [v for (_, k), v in rows.items() if "w4_gemm_kernel" in k]
+        gemm = [v for (_, k), v in rows.items() if "w4t_gemm_kernel" in k]
         red = [v for (_, k), v in rows.items() if "sk_reduce_kernel" in k]
         cal = [v for (_, k), v in rows.items() if "neg" in k.lower()]
         if not gemm or len(cal) != 1:
@@ -236,7 +236,7 @@ def pmc_summary(fetch_dir, write_dir):
                         "bytes_gemm": g, "bytes_reduce": r, "dispatches": len(gemm)}
     alg = gate_up_bytes(cfg)
     hbm = sum(v["bytes_gemm"] + v["bytes_reduce"] for v in out.values())
-    d = {"kernel": "w4_gemm_kernel<T=64, int4, EPI_SWIGLU> + sk_reduce_kernel (gate_up 37888x3584, T=64)",
+    d = {"kernel": "w4t_gemm_kernel<T=64, EPI_SWIGLU> + sk_reduce_kernel (tiled int4 gate_up 37888x3584, T=64)",
          "source_hash": kernel_source_hash(), "alg_bytes_per_launch": int(alg),
          "hbm_bytes_per_launch": int(hbm), "hbm_over_alg": round(hbm / alg, 4), "counters": out}
     with open(PMC_JSON, "w") as fh:
@@ -400,14 +400,14 @@ def main():
     rot = [draft.layers[i % n_layers]["gate_up"] for i in range(8)]
     ks = torch.cuda.Stream()
     with torch.cuda.stream(ks):
-        for q, s, z in rot:
-            bq.w4a16_gate_up_swiglu(x, q, s, z, out=u)
+        for tw in rot:
+            bq.w4a16_gate_up_swiglu_tiled(x, tw, out=u)
         k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         k0.record(ks)
         n_launch = 0
         for _ in range(args.kernel_reps):
-            for q, s, z in rot:
-                bq.w4a16_gate_up_swiglu(x, q, s, z, out=u)
+            for tw in rot:
+                bq.w4a16_gate_up_swiglu_tiled(x, tw, out=u)
                 n_launch += 1
         k1.record(ks)
     torch.cuda.synchronize()
@@ -432,7 +432,7 @@ def main():
                    "draft_step_ms": round(ms_draft_step, 4), "verify_ms": round(ms_verify, 4),
                    "draft_step_alg_bytes": int(step_bytes),
                    "draft_step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4)},
-        "roofline": {"kernel": "w4_gemm_kernel<T=64, int4, EPI_SWIGLU> + sk_reduce_kernel (gate_up 37888x3584, T=64)",
+        "roofline": {"kernel": "w4t_gemm_kernel<T=64, EPI_SWIGLU> + sk_reduce_kernel (tiled int4 gate_up 37888x3584, T=64)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profile(gu_bytes),

@@ -19,6 +19,7 @@ STATUS_NAMES = {0: "SS_OK", -1: "SS_ERR_INVALID_ARG", -2: "SS_ERR_UNSUPPORTED",
 
 SS_W4G64 = 0
 SS_BF16 = 1
+SS_W4G64_TILED = 2
 
 
 class SsLinear(ctypes.Structure):
@@ -68,6 +69,12 @@ SIGNATURES = {
     "ss_w4a16_gate_up_swiglu_workspace": (c_size_t, [c_int32, c_int64, c_int64]),
     "ss_w4a16_gate_up_swiglu": (c_int, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_int64,
                                         c_int64, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "ss_w4_tiled_bytes": (c_size_t, [c_int64, c_int64]),
+    "ss_w4_tile": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_void_p]),
+    "ss_w4a16_linear_tiled": (c_int, [c_void_p, c_int32, c_void_p, c_int64, c_int64, c_void_p, c_void_p,
+                                      c_void_p, c_size_t, c_void_p]),
+    "ss_w4a16_gate_up_swiglu_tiled": (c_int, [c_void_p, c_int32, c_void_p, c_int64, c_int64, c_void_p,
+                                              c_void_p, c_size_t, c_void_p]),
     "ss_bf16_linear_workspace": (c_size_t, [c_int32, c_int64, c_int64]),
     "ss_bf16_linear": (c_int, [c_void_p, c_int32, c_void_p, c_int64, c_int64, c_void_p, c_void_p,
                                c_void_p, c_size_t, c_void_p]),

@@ -10,7 +10,7 @@ import ctypes
 
 import torch
 
-from ._lib import (SS_BF16, SS_W4G64, SsAttnArgs, SsLayer, SsLinear, SsModel, SsStepArgs,
+from ._lib import (SS_BF16, SS_W4G64, SS_W4G64_TILED, SsAttnArgs, SsLayer, SsLinear, SsModel, SsStepArgs,
                    SubspecError, check, lib)
 
 
@@ -61,6 +61,27 @@ def dequantize_substitute(q, s, z, group=64):
     return out
 
 
+class TiledW4:
+    """An int4 weight [n][k] in the tiled layout the GEMMs stream (a relocation of the
+    codes, scales and zeros; see ss_w4_tile in include/subspec.h)."""
+
+    def __init__(self, data, n, k):
+        self.data, self.n, self.k = data, n, k
+
+
+def w4_tile(q, s, z):
+    """(qweight, scale, zero) of an int4 weight [n][k] -> TiledW4."""
+    _need(q, torch.uint8, "qweight")
+    n, kh = q.shape
+    k = kh * 2
+    nbytes = lib().ss_w4_tiled_bytes(n, k)
+    if nbytes == 0:
+        raise SubspecError(f"w4_tile: unsupported shape n={n} k={k}")
+    t = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    check(lib().ss_w4_tile(_ptr(q), _ptr(s), _ptr(z), n, k, _ptr(t), _stream()))
+    return TiledW4(t, n, k)
+
+
 # ------------------------------------------------------------------ linear layers
 
 def w4a16_linear(x, q, s, z, want_bf16=True, want_f32=True, workspace=None):
@@ -87,6 +108,33 @@ def w4a16_gate_up_swiglu(x, q, s, z, out=None, workspace=None):
     ws = _workspace(nbytes, x.device, workspace)
     check(lib().ss_w4a16_gate_up_swiglu(_ptr(x), T, _ptr(q), _ptr(s), _ptr(z), I, k, _ptr(u),
                                         _ptr(ws), nbytes, _stream()))
+    return u
+
+
+def w4a16_linear_tiled(x, tw, want_bf16=True, want_f32=True, workspace=None):
+    """w4a16_linear on a TiledW4 weight."""
+    _need(x, torch.bfloat16, "x")
+    T, k = x.shape
+    n = tw.n
+    yb = torch.empty((T, n), dtype=torch.bfloat16, device=x.device) if want_bf16 else None
+    yf = torch.empty((T, n), dtype=torch.float32, device=x.device) if want_f32 else None
+    nbytes = lib().ss_w4a16_linear_workspace(T, n, k)
+    ws = _workspace(nbytes, x.device, workspace)
+    check(lib().ss_w4a16_linear_tiled(_ptr(x), T, _ptr(tw.data), n, k, _ptr(yb), _ptr(yf), _ptr(ws),
+                                      nbytes, _stream()))
+    return yb, yf
+
+
+def w4a16_gate_up_swiglu_tiled(x, tw, out=None, workspace=None):
+    """w4a16_gate_up_swiglu on a TiledW4 weight [2I][k]."""
+    _need(x, torch.bfloat16, "x")
+    T, k = x.shape
+    I = tw.n // 2
+    u = torch.empty((T, I), dtype=torch.bfloat16, device=x.device) if out is None else out
+    nbytes = lib().ss_w4a16_gate_up_swiglu_workspace(T, I, k)
+    ws = _workspace(nbytes, x.device, workspace)
+    check(lib().ss_w4a16_gate_up_swiglu_tiled(_ptr(x), T, _ptr(tw.data), I, k, _ptr(u), _ptr(ws), nbytes,
+                                              _stream()))
     return u
 
 
@@ -185,7 +233,10 @@ def draft_select(logits, gumbel, inv_temp, k, out=None):
 # ------------------------------------------------------------------ the draft step
 
 def linear_desc(entry):
-    """(qweight, scale, zero) tuple -> int4 descriptor; a bf16 tensor -> dense descriptor."""
+    """(qweight, scale, zero) tuple -> int4 descriptor; TiledW4 -> tiled int4 descriptor;
+    a bf16 tensor -> dense descriptor."""
+    if isinstance(entry, TiledW4):
+        return SsLinear(kind=SS_W4G64_TILED, qweight=entry.data.data_ptr(), scale=None, zero=None, w=None)
     if isinstance(entry, tuple):
         q, s, z = entry
         return SsLinear(kind=SS_W4G64, qweight=q.data_ptr(), scale=s.data_ptr(), zero=z.data_ptr(),
@@ -250,6 +301,6 @@ class SubstituteModel:
 
 
 __all__ = ["abi_version", "quantize_substitute", "dequantize_substitute", "w4a16_linear",
-           "w4a16_gate_up_swiglu",
+           "w4a16_gate_up_swiglu", "TiledW4", "w4_tile", "w4a16_linear_tiled", "w4a16_gate_up_swiglu_tiled",
            "bf16_linear", "tree_validate", "tree_mask", "tree_attention", "row_argmax",
            "tree_accept", "draft_select", "SubstituteModel", "SubspecError"]

@@ -122,6 +122,9 @@ ss::GemmArgs gemm_args(const void* x, int T, const ss_linear& w, int N, int K) {
     a.qw = static_cast<const uint8_t*>(w.qweight);
     a.sc = static_cast<const uint16_t*>(w.scale);
     a.zp = static_cast<const uint16_t*>(w.zero);
+  } else if (w.kind == SS_W4G64_TILED) {
+    a.qw = static_cast<const uint8_t*>(w.qweight);
+    a.tiled = true;
   } else {
     a.wb = static_cast<const uint16_t*>(w.w);
   }
@@ -134,6 +137,9 @@ ss_status check_linear(const char* fn, const ss_linear& w, const char* name) {
       return fail(SS_ERR_INVALID_ARG, "%s: %s: int4 weight, scale and zero must be non-null", fn, name);
     if (!aligned(w.qweight, 16) || !aligned(w.scale, 4) || !aligned(w.zero, 4))
       return fail(SS_ERR_INVALID_ARG, "%s: %s: misaligned int4 weight, scale or zero", fn, name);
+  } else if (w.kind == SS_W4G64_TILED) {
+    if (!w.qweight) return fail(SS_ERR_INVALID_ARG, "%s: %s: tiled int4 weight is null", fn, name);
+    if (!aligned(w.qweight, 16)) return fail(SS_ERR_INVALID_ARG, "%s: %s: tiled int4 weight is not 16-byte aligned", fn, name);
   } else if (w.kind == SS_BF16) {
     if (!w.w) return fail(SS_ERR_INVALID_ARG, "%s: %s: bf16 weight is null", fn, name);
     if (!aligned(w.w, 16)) return fail(SS_ERR_INVALID_ARG, "%s: %s: bf16 weight is not 16-byte aligned", fn, name);
@@ -223,7 +229,7 @@ ss_status check_model(const char* fn, const ss_model* m) {
 extern "C" {
 
 const char* ss_last_error(void) { return g_err.c_str(); }
-int ss_abi_version(void) { return 1; }
+int ss_abi_version(void) { return 2; }
 
 // ------------------------------------------------------------------ quantization
 
@@ -324,6 +330,65 @@ ss_status ss_w4a16_gate_up_swiglu(const void* x_bf16, int32_t T, const void* qwe
   ss_status s = check_device(fn);
   if (s != SS_OK) return s;
   ss_linear w{SS_W4G64, qweight, scale, zero, nullptr};
+  ss::GemmArgs a = gemm_args(x_bf16, T, w, (int)(2 * I), (int)k);
+  a.epi = ss::EPI_SWIGLU;
+  a.swiglu_I = (int)I;
+  a.u_bf16 = static_cast<uint16_t*>(u_bf16);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return launched(fn, ss::launch_gemm(a, pl, workspace, st), st);
+}
+
+size_t ss_w4_tiled_bytes(int64_t n, int64_t k) {
+  if (n <= 0 || k <= 0 || n % 16 || k % 128) return 0;
+  return (size_t)(n / 16) * (size_t)(k / 128) * ss::TILE_BLOCK_BYTES;
+}
+
+ss_status ss_w4_tile(const void* qweight, const void* scale, const void* zero, int64_t n, int64_t k,
+                     void* tiled, void* stream) {
+  const char* fn = __func__;
+  if (n <= 0 || k <= 0) return fail(SS_ERR_INVALID_ARG, "%s: n and k must be positive", fn);
+  if (n % 16 || k % 128) return fail(SS_ERR_UNSUPPORTED, "%s: n must be a multiple of 16 and k of 128", fn);
+  REQ_PTR(qweight, 16); REQ_PTR(scale, 2); REQ_PTR(zero, 2); REQ_PTR(tiled, 16);
+  ss_status s = check_device(fn);
+  if (s != SS_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return launched(fn, ss::launch_w4_tile(static_cast<const uint8_t*>(qweight), static_cast<const uint16_t*>(scale),
+                                         static_cast<const uint16_t*>(zero), n, k, static_cast<uint8_t*>(tiled), st), st);
+}
+
+ss_status ss_w4a16_linear_tiled(const void* x_bf16, int32_t T, const void* tiled, int64_t n, int64_t k,
+                                void* y_bf16, float* y_f32, void* workspace, size_t ws_bytes, void* stream) {
+  const char* fn = __func__;
+  ss_status s = linear_common(fn, x_bf16, T, n, k, y_bf16, y_f32, workspace, ws_bytes);
+  if (s != SS_OK) return s;
+  REQ_PTR(tiled, 16);
+  if ((s = check_device(fn)) != SS_OK) return s;
+  ss_linear w{SS_W4G64_TILED, tiled, nullptr, nullptr, nullptr};
+  ss::GemmArgs a = gemm_args(x_bf16, T, w, (int)n, (int)k);
+  a.epi = ss::EPI_STORE;
+  a.y_f32 = y_f32;
+  a.y_bf16 = static_cast<uint16_t*>(y_bf16);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return launched(fn, ss::launch_gemm(a, ss::plan_gemm(T, (int)n, (int)k, ss::EPI_STORE, 0), workspace, st), st);
+}
+
+ss_status ss_w4a16_gate_up_swiglu_tiled(const void* x_bf16, int32_t T, const void* tiled, int64_t I, int64_t k,
+                                        void* u_bf16, void* workspace, size_t ws_bytes, void* stream) {
+  const char* fn = __func__;
+  if (T < 1 || T > 256) return fail(SS_ERR_UNSUPPORTED, "%s: T must be in 1..256 (got %d)", fn, T);
+  if (I <= 0 || k <= 0) return fail(SS_ERR_INVALID_ARG, "%s: I and k must be positive", fn);
+  if (k % 128) return fail(SS_ERR_UNSUPPORTED, "%s: k must be a multiple of 128", fn);
+  if (I % 16) return fail(SS_ERR_UNSUPPORTED, "%s: I must be a multiple of 16", fn);
+  if (2 * I > 0x7FFFFFFF / 256 || k > 0x7FFFFFFF / 2) return fail(SS_ERR_UNSUPPORTED, "%s: I or k too large", fn);
+  REQ_PTR(x_bf16, 16); REQ_PTR(tiled, 16); REQ_PTR(u_bf16, 2);
+  const ss::GemmPlan pl = ss::plan_gemm(T, (int)(2 * I), (int)k, ss::EPI_SWIGLU, (int)I);
+  if (pl.ws_bytes > 0 && (!workspace || ws_bytes < pl.ws_bytes))
+    return fail(SS_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, pl.ws_bytes,
+                workspace ? ws_bytes : 0);
+  OPT_PTR(workspace, 16);
+  ss_status s = check_device(fn);
+  if (s != SS_OK) return s;
+  ss_linear w{SS_W4G64_TILED, tiled, nullptr, nullptr, nullptr};
   ss::GemmArgs a = gemm_args(x_bf16, T, w, (int)(2 * I), (int)k);
   a.epi = ss::EPI_SWIGLU;
   a.swiglu_I = (int)I;

@@ -608,6 +608,188 @@ __global__ __launch_bounds__((NWC + NLD + 1) * 64) void w4_gemm_kernel(GemmParam
   }
 }
 
+// Tiled int4 weights (TILE_BLOCK_BYTES per 16-row tile and chunk, contiguous): the
+// loader waves stream each chunk's activation fragments AND the block's 8 weight tiles
+// (1 KB of codes each, plus one load for their (scale, zero) words) into the LDS ring
+// with direct-to-LDS loads, so compute waves issue no global loads at all: a compute
+// wave never stalls at a load instruction that the busy address unit has not accepted
+// (waves issue in order, so such a stall would hold back its math). K phases: one.
+// Chunk slots (activations + weights) of the tiled kernel (about 150 KB of LDS at 64
+// tokens; deeper rings for fewer tokens measured no faster).
+constexpr int NS_T = 6;
+
+template <int TT, int EPI>
+__global__ __launch_bounds__((NWC + NLD) * 64) void w4t_gemm_kernel(GemmParams p) {
+  constexpr int RG = NWC;
+  constexpr int FRAG = TT * 4;         // 1 KB activation fragment blocks per chunk
+  constexpr int NT = RG * NR;          // weight tiles per block
+  constexpr int LOADS = FRAG + NT + 1; // loader instructions per chunk
+  constexpr int LA0 = 63 / LOADS < NS_T / NLD ? 63 / LOADS : NS_T / NLD;
+  constexpr int LA = LA0 < 1 ? 1 : LA0;   // chunks in flight per loader
+  static_assert(NT * 8 == 64, "one load carries the (scale, zero) words of all tiles");
+  static_assert(NS_T % NLD == 0, "slot ring must split evenly");
+  __shared__ u32x4_t xfrag[NS_T][4][TT][64];
+  __shared__ u32x4_t wfrag[NS_T][NT][64];
+  __shared__ uint32_t wsz[NS_T][NT * 32];
+  __shared__ int ready[NS_T], done[NS_T];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = blockIdx.x;
+  const SegList L = make_segs(p, g);
+  const int nsegs = L.nd + L.nsk;
+
+  if (tid < NS_T) {
+    ready[tid] = -1;
+    done[tid] = 0;
+  }
+  __syncthreads();   // the only workgroup barrier
+
+  if (wave >= NWC) {
+    // ---------------- loader wave l copies the chunks with sequence number qc = 2 k + l,
+    // keeping LA chunks in flight; before waiting for a slot it drains and publishes
+    // everything it has issued (no consumer can be waiting on a chunk it holds back)
+    const int l = wave - NWC;
+    const int li = lane & 15, lb = lane >> 4;
+    int n = 0, ns = 0, qs = 0;
+    auto publish = [&](int upto) {
+      for (; ns < upto; ++ns) {
+        const int qd = NLD * ns + l;
+        if (lane == 0) lds_store(&ready[qd % NS_T], qd);
+      }
+    };
+    for (int k = 0; k < nsegs; ++k) {
+      int block, s0, s1;
+      seg_of(p, L, g, k, block, s0, s1);
+      const int tb = block % p.tb_count, rb = block / p.tb_count;
+      // global tile of each of the block's weight tiles (rows past N: tile 0, never used)
+      size_t tile_off[NT];
+#pragma unroll
+      for (int i = 0; i < NT; ++i) {
+        const int rgi = i / NR, ri = i % NR;
+        const size_t tile = tile_valid<EPI, RG>(p, rb, rgi, ri) ? (size_t)(tile_row<EPI, RG>(p, rb, rgi, ri, 0) >> 4) : 0;
+        tile_off[i] = tile * p.nchunks * TILE_BLOCK_BYTES;
+      }
+      for (int st = s0; st < s1; ++st, ++qs) {
+        const int qc = qs;
+        if (qc % NLD != l) continue;
+        const int slot = qc % NS_T;
+        if (qc >= NS_T) {
+          const int need = RG * (qc / NS_T);   // the previous occupant was read by all compute waves
+          if (__hip_atomic_load(&done[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < need) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+            publish(n);
+            wait_ge(&done[slot], need);
+          }
+        }
+        const int ch = st;
+        const uint16_t* src = p.x + (size_t)ch * CHUNK_K + lb * 32;
+#pragma unroll
+        for (int ps = 0; ps < FRAG; ++ps) {
+          const int m = ps & 3, tt = ps >> 2;
+          const int tok = min(tb * 64 + tt * 16 + li, p.T - 1);   // padded tokens: clamped copies
+          __builtin_amdgcn_global_load_lds((const void*)(src + (size_t)tok * p.K + m * 8),
+                                           (__attribute__((address_space(3))) void*)&xfrag[slot][m][tt][0],
+                                           16, 0, 0);
+        }
+        const size_t cb = (size_t)ch * TILE_BLOCK_BYTES;
+#pragma unroll
+        for (int i = 0; i < NT; ++i)
+          __builtin_amdgcn_global_load_lds((const void*)(p.qw + tile_off[i] + cb + lane * 16),
+                                           (__attribute__((address_space(3))) void*)&wfrag[slot][i][0], 16, 0, 0);
+        // (scale, zero) words: lane -> tile lane / 8, 16-byte piece lane % 8
+        size_t so = tile_off[0];
+#pragma unroll
+        for (int i = 1; i < NT; ++i)
+          if ((lane >> 3) == i) so = tile_off[i];
+        __builtin_amdgcn_global_load_lds((const void*)(p.qw + so + cb + 1024 + (lane & 7) * 16),
+                                         (__attribute__((address_space(3))) void*)&wsz[slot][0], 16, 0, 0);
+        ++n;
+        if (n - ns > LA) {
+          // all but the newest LA chunks have landed in LDS
+          __builtin_amdgcn_s_waitcnt(((LA * LOADS) & 0xF) | 0x0F70 | (((LA * LOADS) >> 4) << 14));
+          publish(n - LA);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    publish(n);
+    return;
+  }
+
+  // ---------------- compute waves: row group rg = wave
+  const int rg = wave;
+  const int j = lane & 15, b = lane >> 4;
+  f32x4_t acc[NR][TT];
+#pragma unroll
+  for (int r = 0; r < NR; ++r)
+#pragma unroll
+    for (int t = 0; t < TT; ++t) acc[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  int qs = 0;
+  for (int k = 0; k < nsegs; ++k) {
+    int block, s0, s1;
+    seg_of(p, L, g, k, block, s0, s1);
+    for (int st = s0; st < s1; ++st, ++qs) {
+      const int xs = qs % NS_T;
+      wait_eq(&ready[xs], qs);
+      bf16x8_t xa[4][TT];
+      u32x4_t wv[NR];
+      uint32_t szv[NR];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        wv[r] = wfrag[xs][rg * NR + r][lane];
+        szv[r] = wsz[xs][(rg * NR + r) * 32 + j * 2 + (b >> 1)];
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int t = 0; t < TT; ++t) xa[m][t] = __builtin_bit_cast(bf16x8_t, xfrag[xs][m][t][lane]);
+      // every read of the slot has returned before it is released; one increment per wave
+      compiler_fence();
+      lds_wait();
+      if (lane == 0) __hip_atomic_fetch_add(&done[xs], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      float sf[NR], cf[NR], sf16[NR], cf16[NR];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        sf[r] = f16lo(szv[r]);
+        const float zf = f16hi(szv[r]);
+        cf[r] = -(1024.0f + zf) * sf[r];   // 1024 + z is exact in fp32
+        sf16[r] = sf[r] * 0.0625f;         // exact
+        cf16[r] = -(64.0f + zf) * sf[r];
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          const u32x4_t w = wv[r];
+          const u32x4_t d = dequant8(m == 0 ? w.x : m == 1 ? w.y : m == 2 ? w.z : w.w, sf[r], cf[r], sf16[r], cf16[r]);
+#pragma unroll
+          for (int t = 0; t < TT; ++t)
+            acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[m][t], __builtin_bit_cast(bf16x8_t, d), acc[r][t], 0, 0, 0);
+        }
+      }
+    }
+    // end of segment: the result, or the partial of a block split between workgroups
+    if (s0 == 0 && s1 == p.nsteps) {
+      final_store<TT, EPI, RG>(p, acc, block, rg, lane);
+    } else {
+      float* part = p.partials + ((size_t)sk_slot(p, g, block - p.sk_first) * RG + rg) * (NR * TT * 4 * 64);
+#pragma unroll
+      for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) part[((r * TT + t) * 4 + e) * 64 + lane] = acc[r][t][e];
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int t = 0; t < TT; ++t) acc[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
 // Blocks split between workgroups: every thread owns one output element (for SwiGLU,
 // one gate / up pair) of one block, adds the pieces' partials in K order (a fixed
 // order, so results do not depend on timing) and applies the epilogue. A block that
@@ -688,11 +870,13 @@ constexpr int kPF = SS_GEMM_PF;     // int4 weight steps in flight per wave
 constexpr int kPFB = SS_GEMM_PFB;   // bf16 weight steps in flight per wave
 
 template <int TT, bool INT4, int EPI, int KS>
-hipError_t launch_k(const GemmParams& p, int sk_blocks, bool defer, hipStream_t st) {
+hipError_t launch_k(const GemmParams& p, int sk_blocks, bool defer, bool tiled, hipStream_t st) {
   constexpr int PF = INT4 ? kPF : kPFB;
   constexpr bool CAN_SZO = INT4 && KS == 1;
   const bool aligned16 = (reinterpret_cast<uintptr_t>(p.sc) % 16 == 0) && (reinterpret_cast<uintptr_t>(p.zp) % 16 == 0);
-  if (CAN_SZO && p.K % 512 == 0 && aligned16)
+  if (INT4 && KS == 1 && tiled)
+    hipLaunchKernelGGL((w4t_gemm_kernel<TT, EPI>), dim3(p.G), dim3((NWC + NLD) * 64), 0, st, p);
+  else if (CAN_SZO && p.K % 512 == 0 && aligned16)
     hipLaunchKernelGGL((w4_gemm_kernel<TT, INT4, EPI, KS, PF, CAN_SZO>), dim3(p.G), dim3((NWC + NLD + 1) * 64), 0, st, p);
   else
     hipLaunchKernelGGL((w4_gemm_kernel<TT, INT4, EPI, KS, PF, false>), dim3(p.G), dim3((NWC + NLD) * 64), 0, st, p);
@@ -704,19 +888,19 @@ hipError_t launch_k(const GemmParams& p, int sk_blocks, bool defer, hipStream_t 
 }
 
 template <bool INT4, int EPI, int KS>
-hipError_t launch_tt(const GemmParams& p, int TT, int skb, bool defer, hipStream_t st) {
+hipError_t launch_tt(const GemmParams& p, int TT, int skb, bool defer, bool tiled, hipStream_t st) {
   switch (TT) {
-    case 1: return launch_k<1, INT4, EPI, KS>(p, skb, defer, st);
-    case 2: return launch_k<2, INT4, EPI, KS>(p, skb, defer, st);
-    case 3: return launch_k<3, INT4, EPI, KS>(p, skb, defer, st);
-    default: return launch_k<4, INT4, EPI, KS>(p, skb, defer, st);
+    case 1: return launch_k<1, INT4, EPI, KS>(p, skb, defer, tiled, st);
+    case 2: return launch_k<2, INT4, EPI, KS>(p, skb, defer, tiled, st);
+    case 3: return launch_k<3, INT4, EPI, KS>(p, skb, defer, tiled, st);
+    default: return launch_k<4, INT4, EPI, KS>(p, skb, defer, tiled, st);
   }
 }
 
 template <int EPI>
-hipError_t launch_epi(const GemmParams& p, bool int4, int TT, int KS, int skb, bool defer, hipStream_t st) {
-  if (KS == 1) return int4 ? launch_tt<true, EPI, 1>(p, TT, skb, defer, st) : launch_tt<false, EPI, 1>(p, TT, skb, defer, st);
-  return int4 ? launch_tt<true, EPI, 2>(p, TT, skb, defer, st) : launch_tt<false, EPI, 2>(p, TT, skb, defer, st);
+hipError_t launch_epi(const GemmParams& p, bool int4, int TT, int KS, int skb, bool defer, bool tiled, hipStream_t st) {
+  if (KS == 1) return int4 ? launch_tt<true, EPI, 1>(p, TT, skb, defer, tiled, st) : launch_tt<false, EPI, 1>(p, TT, skb, defer, tiled, st);
+  return int4 ? launch_tt<true, EPI, 2>(p, TT, skb, defer, tiled, st) : launch_tt<false, EPI, 2>(p, TT, skb, defer, tiled, st);
 }
 
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
@@ -764,10 +948,13 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& pl, void* ws, hipStrea
   p.partials = pl.sk_blocks > 0 ? reinterpret_cast<float*>(ws) : nullptr;
   const bool int4 = a.qw != nullptr;
   const bool defer = a.defer_reduce && a.epi != EPI_SWIGLU;
+  // the tiled kernel has one K phase; plan_gemm's default (KS = 1) is what it needs
+  const bool tiled = int4 && a.tiled;
+  if (tiled && pl.KS != 1) return hipErrorInvalidValue;
   switch (a.epi) {
-    case EPI_RESID: return launch_epi<EPI_RESID>(p, int4, pl.TT, pl.KS, pl.sk_blocks, defer, st);
-    case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(p, int4, pl.TT, pl.KS, pl.sk_blocks, false, st);
-    default: return launch_epi<EPI_STORE>(p, int4, pl.TT, pl.KS, pl.sk_blocks, defer, st);
+    case EPI_RESID: return launch_epi<EPI_RESID>(p, int4, pl.TT, pl.KS, pl.sk_blocks, defer, tiled, st);
+    case EPI_SWIGLU: return launch_epi<EPI_SWIGLU>(p, int4, pl.TT, pl.KS, pl.sk_blocks, false, tiled, st);
+    default: return launch_epi<EPI_STORE>(p, int4, pl.TT, pl.KS, pl.sk_blocks, defer, tiled, st);
   }
 }
 

@@ -11,6 +11,10 @@ namespace ss {
 
 enum Epilogue { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
 
+// Tiled int4 layout: per (16-row tile, 128-wide K chunk) one block of 1 KB of codes in
+// the GEMM's lane order followed by 16 rows x 2 groups of (scale, zero) fp16 pairs.
+constexpr int TILE_BLOCK_BYTES = 1024 + 16 * 2 * 4;
+
 struct GemmArgs {
   const uint16_t* x;   // bf16 [T][K]
   const uint8_t* qw;   // int4 weights, or null for bf16 weights
@@ -25,6 +29,7 @@ struct GemmArgs {
   float* resid;
   uint16_t* u_bf16;
   bool defer_reduce;   // leave split blocks' partials for the consumer (see SplitView)
+  bool tiled;          // qw holds the tiled layout (TILE_BLOCK_BYTES per tile and chunk)
 };
 
 // Decomposition of one GEMM call: row blocks x token blocks, each cut into steps of KS
@@ -66,6 +71,8 @@ hipError_t launch_quantize_g64(const uint16_t* w, int64_t n, int64_t k, uint8_t*
                                uint16_t* z, hipStream_t st);
 hipError_t launch_dequantize_g64(const uint8_t* q, const uint16_t* s, const uint16_t* z, int64_t n,
                                  int64_t k, uint16_t* out, hipStream_t st);
+hipError_t launch_w4_tile(const uint8_t* q, const uint16_t* s, const uint16_t* z, int64_t n, int64_t k,
+                          uint8_t* tiled, hipStream_t st);
 
 // tree + attention
 hipError_t launch_tree_mask(const int32_t* parents, int T, uint64_t* mask, int32_t* depth,

@@ -94,6 +94,47 @@ __global__ __launch_bounds__(256) void dequantize_g64_kernel(const uint32_t* __r
   }
 }
 
+// Relocation into the tiled layout, block (tile i, chunk c). One thread per 16-byte
+// unit: unit l < 64 holds the codes of lane l (row 16 i + l % 16, code bytes
+// 64 c + 16 (l / 16) .. +15 of that row); unit 64 + w holds the (scale, zero) words
+// 4 w .. 4 w + 3, word 2 j + h being scale | zero << 16 of row 16 i + j, group 2 c + h.
+__global__ __launch_bounds__(256) void w4_tile_kernel(const uint8_t* __restrict__ q, const uint16_t* __restrict__ s,
+                                                      const uint16_t* __restrict__ z, int64_t n, int64_t k,
+                                                      uint8_t* __restrict__ tiled) {
+  constexpr int UNITS = TILE_BLOCK_BYTES / 16;   // 72
+  const int64_t nchunks = k >> 7, G = k >> 6;
+  const int64_t total = (n >> 4) * nchunks * UNITS;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t blk = idx / UNITS;
+    const int u = (int)(idx - blk * UNITS);
+    const int64_t tile = blk / nchunks, c = blk - tile * nchunks;
+    u32x4_t v;
+    if (u < 64) {
+      const int64_t row = tile * 16 + (u & 15);
+      v = *reinterpret_cast<const u32x4_t*>(q + row * (k >> 1) + c * 64 + (u >> 4) * 16);
+    } else {
+      uint32_t w4[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int word = (u - 64) * 4 + e;   // 2 j + h
+        const int64_t gi = (tile * 16 + (word >> 1)) * G + 2 * c + (word & 1);
+        w4[e] = (uint32_t)s[gi] | ((uint32_t)z[gi] << 16);
+      }
+      v = u32x4_t{w4[0], w4[1], w4[2], w4[3]};
+    }
+    *reinterpret_cast<u32x4_t*>(tiled + blk * TILE_BLOCK_BYTES + u * 16) = v;
+  }
+}
+
+hipError_t launch_w4_tile(const uint8_t* q, const uint16_t* s, const uint16_t* z, int64_t n, int64_t k,
+                          uint8_t* tiled, hipStream_t st) {
+  const int64_t units = (n >> 4) * (k >> 7) * (TILE_BLOCK_BYTES / 16);
+  const int64_t blocks = std::min<int64_t>((units + 255) / 256, 65536);
+  hipLaunchKernelGGL(w4_tile_kernel, dim3((unsigned)blocks), dim3(256), 0, st, q, s, z, n, k, tiled);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize_g64(const uint16_t* w, int64_t n, int64_t k, uint8_t* q, uint16_t* s,
                                uint16_t* z, hipStream_t st) {
   const int64_t groups = n * (k >> 6);

@@ -94,6 +94,26 @@ ss_status ss_w4a16_gate_up_swiglu(const void* x_bf16, int32_t T, const void* qwe
                                   const void* scale, const void* zero, int64_t I, int64_t k,
                                   void* u_bf16, void* workspace, size_t ws_bytes, void* stream);
 
+/* Tiled int4 layout (a relocation of qweight / scale / zero, values unchanged), read
+ * by the GEMMs as one contiguous 1152-byte block per 16-row tile i (rows 16 i ..
+ * 16 i + 15) and 128-wide K chunk c, at byte (i * k/128 + c) * 1152:
+ *   bytes 16 l .. 16 l + 15 (l = 0..63): code bytes 64 c + 16 (l / 16) .. +15 of row
+ *     16 i + l % 16 (its elements k = 128 c + 32 (l / 16) .. +31);
+ *   bytes 1024 + 4 (2 j + h) (j = 0..15, h = 0, 1): the fp16 scale (low half) and the
+ *     fp16 zero (high half) of row 16 i + j, group 2 c + h.
+ * ss_w4_tiled_bytes gives the size, n/16 * k/128 * 1152 (0 for unsupported shapes).
+ * n % 16 == 0, k % 128 == 0. The _tiled linears compute exactly what the untiled ones
+ * compute from the same weights. */
+size_t ss_w4_tiled_bytes(int64_t n, int64_t k);
+ss_status ss_w4_tile(const void* qweight, const void* scale, const void* zero, int64_t n, int64_t k,
+                     void* tiled, void* stream);
+ss_status ss_w4a16_linear_tiled(const void* x_bf16, int32_t T, const void* tiled, int64_t n, int64_t k,
+                                void* y_bf16, float* y_f32, void* workspace, size_t ws_bytes,
+                                void* stream);
+ss_status ss_w4a16_gate_up_swiglu_tiled(const void* x_bf16, int32_t T, const void* tiled, int64_t I,
+                                        int64_t k, void* u_bf16, void* workspace, size_t ws_bytes,
+                                        void* stream);
+
 /* Dense bf16-weight linear layer, for layers the draft shares with the target
  * unquantized ([Review] §2.2 step 4: layers that fit on the GPU stay shared with the
  * target; here the LM head) and for the target verify pass. W bf16 [n][k]; otherwise
@@ -155,11 +175,11 @@ ss_status ss_tree_attention(const ss_attn_args* args, void* workspace, size_t ws
  * kernel boundaries. Reading (the pages give no layer): the pre-norm Qwen2.5 /
  * Llama-3.1 decoder layer, no qkv bias.
  * ------------------------------------------------------------------------------ */
-typedef enum { SS_W4G64 = 0, SS_BF16 = 1 } ss_weight_kind;
+typedef enum { SS_W4G64 = 0, SS_BF16 = 1, SS_W4G64_TILED = 2 } ss_weight_kind;
 
 typedef struct {
   int32_t kind;          /* ss_weight_kind */
-  const void* qweight;   /* SS_W4G64: u8 [n][k/2] */
+  const void* qweight;   /* SS_W4G64: u8 [n][k/2]; SS_W4G64_TILED: the tiled layout */
   const void* scale;     /* SS_W4G64: fp16 [n][k/64] */
   const void* zero;      /* SS_W4G64: fp16 [n][k/64] */
   const void* w;         /* SS_BF16: bf16 [n][k] */
