@@ -242,7 +242,7 @@ def pmc_summary(fetch_dir, write_dir):
     with open(PMC_JSON, "w") as fh:
         json.dump(d, fh, indent=1)
     lines = [
-        "# gate_up + SwiGLU (int4 g64, 37888 x 3584, T=64): HBM traffic from PMC counters",
+        "# Tiled int4 gate_up + SwiGLU (g64, 37888 x 3584, T=64): HBM traffic from PMC counters",
         "",
         "Commands (from the repository root on the GPU host; each pass its own run):",
         "",
