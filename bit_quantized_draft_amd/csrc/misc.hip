@@ -132,33 +132,33 @@ __global__ __launch_bounds__(256) void rope_split_kernel(const float* __restrict
 
 // ------------------------------------------------------------------ fused split finish
 
-#ifndef SS_SV_THREADS
-#define SS_SV_THREADS 1024
-#endif
-constexpr int SV_THREADS = SS_SV_THREADS;
+constexpr int SV_THREADS = 256;      // qkv split finish: threads per part of a row
+constexpr int SV_PARTS = 4;          // qkv split finish: parts (head ranges) per row
 constexpr int SV_MAX_BLOCKS = 128;   // row blocks per token row
-constexpr int SV_MAX_W = 8192;       // row width
-static_assert(SV_THREADS * 8 >= SV_MAX_W, "the largest KM (8) must cover a row");
+constexpr int SV_MAX_PART = SV_THREADS * 8;   // columns per part (the largest KM is 8)
+constexpr int RN_THREADS = 1024;     // residual split finish + RMSNorm: one workgroup per row
+constexpr int RN_MAX_W = RN_THREADS * 8;
 
 // One workgroup per token row: finish the split blocks of a residual GEMM into h32[t]
 // (h += sum of pieces; blocks the GEMM stored itself are already in h32), then, when gain
-// is given, the row's RMSNorm into xn.
+// is given, the row's RMSNorm into xn. (Spreading a row over several workgroups needs a
+// device-scope hand-off for the norm; its fences cost more than the row's loads.)
 template <int KM>
-__global__ __launch_bounds__(SV_THREADS) void resid_norm_kernel(SplitView v, float* __restrict__ h32, int H,
+__global__ __launch_bounds__(RN_THREADS) void resid_norm_kernel(SplitView v, float* __restrict__ h32, int H,
                                                                 const uint16_t* __restrict__ gain, float eps,
                                                                 uint16_t* __restrict__ xn) {
   __shared__ SvBlock blk[SV_MAX_BLOCKS];
-  __shared__ float red[SV_THREADS / 64];
+  __shared__ float red[RN_THREADS / 64];
   const int t = blockIdx.x, tb = t >> 6;
   for (int rb = threadIdx.x; rb < v.rb_count; rb += blockDim.x) blk[rb] = sv_block(v, tb + rb * v.tb_count);
   __syncthreads();
   float* row = h32 + (size_t)t * H;
   float hv[KM];
-  sv_row<KM>(v, blk, t, H, row, true, hv);
+  sv_row<KM>(v, blk, t, 0, H, row, true, hv);
   float ss = 0.f;
 #pragma unroll
   for (int k = 0; k < KM; ++k) {
-    const int n = k * SV_THREADS + threadIdx.x;
+    const int n = k * RN_THREADS + threadIdx.x;
     if (n < H) {
       const SvBlock b = blk[n / v.rows_per_block];
       if (b.g1 != b.g0) row[n] = hv[k];
@@ -171,19 +171,20 @@ __global__ __launch_bounds__(SV_THREADS) void resid_norm_kernel(SplitView v, flo
   __syncthreads();
   float tot = 0.f;
 #pragma unroll
-  for (int w = 0; w < SV_THREADS / 64; ++w) tot += red[w];
+  for (int w = 0; w < RN_THREADS / 64; ++w) tot += red[w];
   const float rs = 1.0f / sqrtf(tot / (float)H + eps);
   uint16_t* o = xn + (size_t)t * H;
 #pragma unroll
   for (int k = 0; k < KM; ++k) {
-    const int n = k * SV_THREADS + threadIdx.x;
+    const int n = k * RN_THREADS + threadIdx.x;
     if (n < H) o[n] = f32_to_bf16(hv[k] * rs * bf16_to_f32(gain[n]));
   }
 }
 
-// One workgroup per token row: finish the split qkv blocks into LDS, then RoPE
-// (rotate-half) on q and k at position C + depth[t] with fp64 angles, and scatter to q
-// [T][nq][hd] and tree K / V [nkv][T][hd] (bf16).
+// Workgroup (t, part) finishes the split qkv blocks of heads [h0, h1) of row t into LDS,
+// then applies RoPE (rotate-half) to its q and k heads at position C + depth[t] with fp64
+// angles and scatters to q [T][nq][hd] and tree K / V [nkv][T][hd] (bf16). RoPE stays
+// inside a head, so the parts are independent.
 template <int KM>
 __global__ __launch_bounds__(SV_THREADS) void qkv_rope_kernel(SplitView v, const float* __restrict__ qkv,
                                                               const int32_t* __restrict__ depth, int T, int C,
@@ -191,11 +192,14 @@ __global__ __launch_bounds__(SV_THREADS) void qkv_rope_kernel(SplitView v, const
                                                               uint16_t* __restrict__ q, uint16_t* __restrict__ kt,
                                                               uint16_t* __restrict__ vt) {
   __shared__ SvBlock blk[SV_MAX_BLOCKS];
-  __shared__ float rowv[SV_MAX_W];
+  __shared__ float rowv[SV_MAX_PART];
   __shared__ float cs[64], sn[64];   // hd <= 128
-  const int t = blockIdx.x, tb = t >> 6;
+  const int t = blockIdx.x, part = blockIdx.y, tb = t >> 6;
   const int half = hd >> 1;
-  const int W = (nq + 2 * nkv) * hd;
+  const int NH = nq + 2 * nkv;
+  const int h0 = part * NH / SV_PARTS, h1 = (part + 1) * NH / SV_PARTS;
+  const int W = NH * hd;
+  const int c0 = h0 * hd, c1 = h1 * hd;
   for (int rb = threadIdx.x; rb < v.rb_count; rb += blockDim.x) blk[rb] = sv_block(v, tb + rb * v.tb_count);
   if (threadIdx.x < half) {
     const double pos = (double)(C + depth[t]);
@@ -207,35 +211,37 @@ __global__ __launch_bounds__(SV_THREADS) void qkv_rope_kernel(SplitView v, const
   }
   __syncthreads();
   float val[KM];
-  sv_row<KM>(v, blk, t, W, qkv + (size_t)t * W, false, val);
+  sv_row<KM>(v, blk, t, c0, c1, qkv + (size_t)t * W, false, val);
 #pragma unroll
   for (int k = 0; k < KM; ++k) {
-    const int n = k * SV_THREADS + threadIdx.x;
-    if (n < W) rowv[n] = val[k];
+    const int n = c0 + k * SV_THREADS + threadIdx.x;
+    if (n < c1) rowv[n - c0] = val[k];
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < (nq + nkv) * half; e += blockDim.x) {
-    const int h = e / half, i = e - h * half;
+  const int hr = min(h1, nq + nkv);   // rotated heads of this part: [h0, hr)
+  for (int e = threadIdx.x; e < (hr - h0) * half; e += blockDim.x) {
+    const int h = h0 + e / half, i = e % half;
     const float c = cs[i], s = sn[i];
-    const float a = rowv[h * hd + i], bb = rowv[h * hd + i + half];
+    const float a = rowv[(h - h0) * hd + i], bb = rowv[(h - h0) * hd + i + half];
     const float r0 = a * c - bb * s;
     const float r1 = bb * c + a * s;
     uint16_t* dst = (h < nq) ? q + ((size_t)t * nq + h) * hd : kt + ((size_t)(h - nq) * T + t) * hd;
     dst[i] = f32_to_bf16(r0);
     dst[i + half] = f32_to_bf16(r1);
   }
-  for (int i = threadIdx.x; i < nkv * hd; i += blockDim.x) {
-    const int kh = i / hd, d = i % hd;
-    vt[((size_t)kh * T + t) * hd + d] = f32_to_bf16(rowv[(nq + nkv) * hd + i]);
+  const int hv0 = max(h0, nq + nkv);   // value heads of this part: [hv0, h1)
+  for (int e = threadIdx.x; e < (h1 - hv0) * hd; e += blockDim.x) {
+    const int h = hv0 + e / hd, d = e % hd;
+    vt[((size_t)(h - nq - nkv) * T + t) * hd + d] = f32_to_bf16(rowv[(h - h0) * hd + d]);
   }
 }
 
 namespace {
-int sv_km(int W) {
-  const int need = (W + SV_THREADS - 1) / SV_THREADS;
+int sv_km(int width) {
+  const int need = (width + SV_THREADS - 1) / SV_THREADS;
   return need <= 2 ? 2 : need <= 4 ? 4 : need <= 6 ? 6 : 8;
 }
-// the kernels' 32-bit ownership arithmetic and their per-thread element count
+// the kernels' 32-bit ownership arithmetic
 bool sv_fits(const SplitView& v) {
   return v.sk_units * (long long)std::max(v.G_sk, 1) < (1LL << 31) && v.nsteps > 0;
 }
@@ -243,12 +249,14 @@ bool sv_fits(const SplitView& v) {
 
 hipError_t launch_resid_norm(const SplitView& v, float* h32, int T, int H, const uint16_t* gain,
                              float eps, uint16_t* xn, hipStream_t st) {
-  if (H > SV_MAX_W || v.rb_count > SV_MAX_BLOCKS || !sv_fits(v)) return hipErrorInvalidValue;
-  switch (sv_km(H)) {
-    case 2: hipLaunchKernelGGL(resid_norm_kernel<2>, dim3(T), dim3(SV_THREADS), 0, st, v, h32, H, gain, eps, xn); break;
-    case 4: hipLaunchKernelGGL(resid_norm_kernel<4>, dim3(T), dim3(SV_THREADS), 0, st, v, h32, H, gain, eps, xn); break;
-    case 6: hipLaunchKernelGGL(resid_norm_kernel<6>, dim3(T), dim3(SV_THREADS), 0, st, v, h32, H, gain, eps, xn); break;
-    default: hipLaunchKernelGGL(resid_norm_kernel<8>, dim3(T), dim3(SV_THREADS), 0, st, v, h32, H, gain, eps, xn); break;
+  if (H > RN_MAX_W || v.rb_count > SV_MAX_BLOCKS || !sv_fits(v)) return hipErrorInvalidValue;
+  const int need = (H + RN_THREADS - 1) / RN_THREADS;
+  const int km = need <= 2 ? 2 : need <= 4 ? 4 : need <= 6 ? 6 : 8;
+  switch (km) {
+    case 2: hipLaunchKernelGGL(resid_norm_kernel<2>, dim3(T), dim3(RN_THREADS), 0, st, v, h32, H, gain, eps, xn); break;
+    case 4: hipLaunchKernelGGL(resid_norm_kernel<4>, dim3(T), dim3(RN_THREADS), 0, st, v, h32, H, gain, eps, xn); break;
+    case 6: hipLaunchKernelGGL(resid_norm_kernel<6>, dim3(T), dim3(RN_THREADS), 0, st, v, h32, H, gain, eps, xn); break;
+    default: hipLaunchKernelGGL(resid_norm_kernel<8>, dim3(T), dim3(RN_THREADS), 0, st, v, h32, H, gain, eps, xn); break;
   }
   return hipGetLastError();
 }
@@ -256,14 +264,16 @@ hipError_t launch_resid_norm(const SplitView& v, float* h32, int T, int H, const
 hipError_t launch_qkv_rope(const SplitView& v, const float* qkv32, const int32_t* depth, int T, int C,
                            int nq, int nkv, int hd, float theta, uint16_t* q, uint16_t* kt,
                            uint16_t* vt, hipStream_t st) {
-  const int W = (nq + 2 * nkv) * hd;
-  if (W > SV_MAX_W || v.rb_count > SV_MAX_BLOCKS || hd > 128 || !sv_fits(v)) return hipErrorInvalidValue;
+  const int NH = nq + 2 * nkv;
+  const int width = ((NH + SV_PARTS - 1) / SV_PARTS) * hd;   // the widest part
+  if (width > SV_MAX_PART || v.rb_count > SV_MAX_BLOCKS || hd > 128 || !sv_fits(v)) return hipErrorInvalidValue;
   const double th = theta;
-  switch (sv_km(W)) {
-    case 2: hipLaunchKernelGGL(qkv_rope_kernel<2>, dim3(T), dim3(SV_THREADS), 0, st, v, qkv32, depth, T, C, nq, nkv, hd, th, q, kt, vt); break;
-    case 4: hipLaunchKernelGGL(qkv_rope_kernel<4>, dim3(T), dim3(SV_THREADS), 0, st, v, qkv32, depth, T, C, nq, nkv, hd, th, q, kt, vt); break;
-    case 6: hipLaunchKernelGGL(qkv_rope_kernel<6>, dim3(T), dim3(SV_THREADS), 0, st, v, qkv32, depth, T, C, nq, nkv, hd, th, q, kt, vt); break;
-    default: hipLaunchKernelGGL(qkv_rope_kernel<8>, dim3(T), dim3(SV_THREADS), 0, st, v, qkv32, depth, T, C, nq, nkv, hd, th, q, kt, vt); break;
+  const dim3 grid(T, SV_PARTS);
+  switch (sv_km(width)) {
+    case 2: hipLaunchKernelGGL(qkv_rope_kernel<2>, grid, dim3(SV_THREADS), 0, st, v, qkv32, depth, T, C, nq, nkv, hd, th, q, kt, vt); break;
+    case 4: hipLaunchKernelGGL(qkv_rope_kernel<4>, grid, dim3(SV_THREADS), 0, st, v, qkv32, depth, T, C, nq, nkv, hd, th, q, kt, vt); break;
+    case 6: hipLaunchKernelGGL(qkv_rope_kernel<6>, grid, dim3(SV_THREADS), 0, st, v, qkv32, depth, T, C, nq, nkv, hd, th, q, kt, vt); break;
+    default: hipLaunchKernelGGL(qkv_rope_kernel<8>, grid, dim3(SV_THREADS), 0, st, v, qkv32, depth, T, C, nq, nkv, hd, th, q, kt, vt); break;
   }
   return hipGetLastError();
 }

@@ -41,8 +41,8 @@ __device__ __forceinline__ size_t sv_offset(const SplitView& v, int t, int n) {
   return (size_t)rg * (2 * v.TT * 256) + ((r * v.TT + tt) * 4 + e) * 64 + 16 * bq + j;
 }
 
-// Final values of one token row's elements n = k * blockDim.x + threadIdx.x (k < KM,
-// n < W). blk holds the row's block table (one entry per row block). A split element is
+// Final values of one token row's elements n = c0 + k * blockDim.x + threadIdx.x (k < KM,
+// n < c1). blk holds the row's block table (one entry per row block). A split element is
 // the sum of its pieces in K order from 0, plus row[n] when add_row (a residual); any
 // other element is row[n] as the GEMM left it. Piece loads go out SV_BATCH at a time per
 // element, all independent, and are added afterwards in order.
@@ -52,7 +52,7 @@ __device__ __forceinline__ size_t sv_offset(const SplitView& v, int t, int n) {
 constexpr int SV_BATCH = SS_SV_BATCH;
 
 template <int KM>
-__device__ __forceinline__ void sv_row(const SplitView& v, const SvBlock* blk, int t, int W,
+__device__ __forceinline__ void sv_row(const SplitView& v, const SvBlock* blk, int t, int c0, int c1,
                                        const float* __restrict__ row, bool add_row, float (&val)[KM]) {
   const size_t se = (size_t)v.RG * 2 * v.TT * 256;   // floats per partial slot
   float s[KM];
@@ -61,8 +61,8 @@ __device__ __forceinline__ void sv_row(const SplitView& v, const SvBlock* blk, i
   int pmax = 0;
 #pragma unroll
   for (int k = 0; k < KM; ++k) {
-    const int n = k * (int)blockDim.x + (int)threadIdx.x;
-    const bool in = n < W;
+    const int n = c0 + k * (int)blockDim.x + (int)threadIdx.x;
+    const bool in = n < c1;
     SvBlock b{0, 0, 0};
     if (in) b = blk[n / v.rows_per_block];
     g0[k] = b.g0;
