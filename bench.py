@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--pmc-probe", action="store_true",
                     help="run only the dominant kernel over rotated weights, then a 256 MiB "
                          "negation as the counter calibration (for rocprofv3 --pmc passes)")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="MFMA utilisation at the large-tree workload: the four tiled int4 linears "
+                         "of a Qwen2.5-32B-shaped layer at T=256, timed against the dense bf16 peak")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) of "
                          "--pmc-probe into the traffic summary under profiles/ (CPU only)")
@@ -198,6 +201,66 @@ def pmc_probe(args):
           flush=True)
 
 
+MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+
+
+def mfma_probe(args):
+    """The substitute GEMMs of one Qwen2.5-32B-shaped layer at T=256 (the large-tree
+    workload, MFMA-bound: 2T/0.5625 = 910 FLOP/B > the 312 FLOP/B ridge), tiled int4
+    weights of two layers in rotation (> 256 MB Infinity Cache), each linear timed with
+    HIP events on its own stream. Reports TFLOP/s against the dense bf16 MFMA peak."""
+    import torch
+    import bit_quantized_draft_amd as bq
+    from synth import gen
+    from synth.configs import get_config, layer_shapes
+    cfg = get_config(4)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    T = cfg.T
+    copies = 2
+    ws = {}
+    for name, N, K in layer_shapes(cfg):
+        ws[name] = []
+        for li in range(copies):
+            w = gen.torch_normal_bf16((N, K), cfg.w_std, 0, cfg.cid, gen.TID_W, li * 16 + gen.SLOT[name], dev)
+            ws[name].append(bq.w4_tile(*bq.quantize_substitute(w)))
+            del w
+    torch.cuda.empty_cache()
+    res = {}
+    tot_flop, tot_us = 0.0, 0.0
+    ks = torch.cuda.Stream()
+    for name, N, K in layer_shapes(cfg):
+        x = gen.torch_normal_bf16((T, K), 1.0, 0, cfg.cid, gen.TID_X, 0, dev)
+        if name == "gate_up":
+            out = torch.empty((T, N // 2), dtype=torch.bfloat16, device=dev)
+            run = lambda tw: bq.w4a16_gate_up_swiglu_tiled(x, tw, out=out)
+        else:
+            run = lambda tw: bq.w4a16_linear_tiled(x, tw, want_bf16=False)
+        with torch.cuda.stream(ks):
+            for tw in ws[name]:
+                run(tw)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(ks)
+            n = 0
+            for _ in range(args.kernel_reps):
+                for tw in ws[name]:
+                    run(tw)
+                    n += 1
+            e1.record(ks)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / n
+        flop = 2.0 * T * N * K
+        tot_flop += flop
+        tot_us += us
+        res[name] = {"N": N, "K": K, "us": round(us, 2), "tflops": round(flop / us / 1e6, 1),
+                     "mfma_frac": round(flop / us / 1e6 / MFMA_PEAK_TFLOPS, 4),
+                     "hbm_gbs": round(0.5625 * N * K / us / 1e3, 1)}
+    line = {"probe": "mfma", "workload": f"{cfg.name} layer GEMMs (tiled int4), T={T}", "peak_tflops": MFMA_PEAK_TFLOPS,
+            "layer_us": round(tot_us, 2), "layer_tflops": round(tot_flop / tot_us / 1e6, 1),
+            "layer_mfma_frac": round(tot_flop / tot_us / 1e6 / MFMA_PEAK_TFLOPS, 4), "gemms": res}
+    print(json.dumps(line), flush=True)
+
+
 def _counter_rows(folder, counter):
     import csv
     import glob
@@ -293,6 +356,9 @@ def main():
         sys.exit(2)
     if args.pmc_probe:
         pmc_probe(args)
+        return
+    if args.mfma_probe:
+        mfma_probe(args)
         return
     import torch
     import bit_quantized_draft_amd as bq
