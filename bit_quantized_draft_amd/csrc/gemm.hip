@@ -746,10 +746,6 @@ __global__ __launch_bounds__((NWC + NLD) * 64) void w4t_gemm_kernel(GemmParams p
       for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int t = 0; t < TT; ++t) xa[m][t] = __builtin_bit_cast(bf16x8_t, xfrag[xs][m][t][lane]);
-      // every read of the slot has returned before it is released; one increment per wave
-      compiler_fence();
-      lds_wait();
-      if (lane == 0) __hip_atomic_fetch_add(&done[xs], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       float sf[NR], cf[NR], sf16[NR], cf16[NR];
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
@@ -770,6 +766,12 @@ __global__ __launch_bounds__((NWC + NLD) * 64) void w4t_gemm_kernel(GemmParams p
             acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[m][t], __builtin_bit_cast(bf16x8_t, d), acc[r][t], 0, 0, 0);
         }
       }
+      // the slot is released after the chunk's math: its reads land while the first k-steps
+      // are multiplied (the compiler waits for each fragment at its first use); every read
+      // has returned before the release; one increment per wave
+      compiler_fence();
+      lds_wait();
+      if (lane == 0) __hip_atomic_fetch_add(&done[xs], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     // end of segment: the result, or the partial of a block split between workgroups
     if (s0 == 0 && s1 == p.nsteps) {
