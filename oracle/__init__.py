@@ -26,7 +26,7 @@ is "parity unpinned" as a whole.
 from .fp import bf16_to_f32, bf16_to_f64, f32_to_bf16  # noqa: F401
 from .quant import quantize, pack_int4, unpack_int4, dequantize_f16, dequant_exact64  # noqa: F401
 from .linalg import matmul64, w4a16_matmul64  # noqa: F401
-from .tree import validate_tree, tree_mask, tree_depth, accept  # noqa: F401
+from .tree import validate_tree, tree_mask, tree_depth, accept, kv_commit  # noqa: F401
 from .attention import tree_attention64, tree_attention_loop64  # noqa: F401
 from .layer import rmsnorm64, rope64, silu64, swiglu64, layer64, stack64  # noqa: F401
 from .select import row_argmax, draft_select  # noqa: F401

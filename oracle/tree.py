@@ -75,3 +75,22 @@ def accept(parents, tokens, target_argmax):
         path.append(nxt)
         cur = nxt
     return path, len(path), int(target_argmax[cur])
+
+
+def kv_commit(k_cache, v_cache, k_tree, v_tree, path, C):
+    """Commit the accepted tokens' keys and values to the shared cache.
+
+    [Review] §4.1: draft and target share one KV cache; the verification of a cycle
+    commits the root and the L accepted nodes (the acceptance walk above). Reading
+    (the pages give no procedure): the target's tree K/V rows of the root and of the
+    accepted path, which already carry RoPE at positions C + depth, are written in path
+    order to cache rows C .. C + L (depth i lands in row C + i); nothing else changes.
+    Arrays hold bf16 bits: caches [nkv][c_stride][hd], tree K/V [nkv][T][hd].
+    Returns new arrays.
+    """
+    k = np.array(k_cache, copy=True)
+    v = np.array(v_cache, copy=True)
+    for i, node in enumerate([0] + [int(n) for n in path]):
+        k[:, C + i, :] = k_tree[:, node, :]
+        v[:, C + i, :] = v_tree[:, node, :]
+    return k, v

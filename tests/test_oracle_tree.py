@@ -159,3 +159,66 @@ def test_golden_tree_example():
     for case in gold["accept_cases"]:
         path, L, bonus = oracle.accept(par, gold["tokens"], case["target_argmax"])
         assert path == case["path"] and L == case["accept_len"] and bonus == case["bonus"]
+
+
+# ------------------------------------------------------------------ KV commit
+
+def _kv_case(T, C, c_stride, nkv=2, hd=64, seed=0, kind="CB"):
+    par = gen.tree_parents(T, kind, seed=seed)
+    tok = gen.tree_tokens(par, 1000, seed=seed)
+    rng = np.random.default_rng(seed)
+    kc = rng.integers(0, 1 << 16, (nkv, c_stride, hd), dtype=np.uint16)
+    vc = rng.integers(0, 1 << 16, (nkv, c_stride, hd), dtype=np.uint16)
+    kt = rng.integers(0, 1 << 16, (nkv, T, hd), dtype=np.uint16)
+    vt = rng.integers(0, 1 << 16, (nkv, T, hd), dtype=np.uint16)
+    return par, tok, kc, vc, kt, vt
+
+
+def test_kv_commit_writes_only_the_committed_rows():
+    T, C, cs = 40, 100, 160
+    par, tok, kc, vc, kt, vt = _kv_case(T, C, cs, seed=3)
+    tgt = gen.target_logits(par, tok, 1000, 9, seed=3).argmax(axis=1)
+    path, L, _ = oracle.accept(par, tok, tgt)
+    assert L == len(path) > 0
+    k2, v2 = oracle.kv_commit(kc, vc, kt, vt, path, C)
+    rows = C + L + 1
+    assert np.array_equal(k2[:, :C], kc[:, :C]) and np.array_equal(k2[:, rows:], kc[:, rows:])
+    assert np.array_equal(v2[:, :C], vc[:, :C]) and np.array_equal(v2[:, rows:], vc[:, rows:])
+    assert np.array_equal(k2[:, C], kt[:, 0]) and np.array_equal(v2[:, C], vt[:, 0])   # the root first
+    for i, node in enumerate(path):
+        assert np.array_equal(k2[:, C + 1 + i], kt[:, node])
+        assert np.array_equal(v2[:, C + 1 + i], vt[:, node])
+    # nothing accepted: only the root is committed
+    k0, _ = oracle.kv_commit(kc, vc, kt, vt, [], C)
+    assert np.array_equal(k0[:, C], kt[:, 0]) and np.array_equal(k0[:, C + 1:], kc[:, C + 1:])
+
+
+def test_kv_commit_matches_attention_over_the_accepted_path():
+    # The accepted path is the ancestor chain of its last node, so that node's tree
+    # attention must equal plain attention (every key visible) over the committed cache:
+    # checked against torch's scaled-dot-product attention, not against the oracle.
+    torch = pytest.importorskip("torch")
+    T, C, nkv, grp, hd = 48, 64, 2, 3, 64
+    par, tok, _, _, _, _ = _kv_case(T, C, C + T, nkv=nkv, hd=hd, seed=5)
+    tgt = gen.target_logits(par, tok, 1000, 20, seed=5).argmax(axis=1)
+    path, L, _ = oracle.accept(par, tok, tgt)
+    assert L >= 10
+    rng = np.random.default_rng(5)
+    bf = lambda a: oracle.f32_to_bf16(a.astype(np.float32))
+    q = bf(rng.standard_normal((T, nkv * grp, hd)))
+    kc = bf(rng.standard_normal((nkv, C + T, hd)))
+    vc = bf(rng.standard_normal((nkv, C + T, hd)))
+    kt = bf(rng.standard_normal((nkv, T, hd)))
+    vt = bf(rng.standard_normal((nkv, T, hd)))
+    f = oracle.bf16_to_f64
+    tree_out = oracle.tree_attention64(f(q), f(kc), f(vc), f(kt), f(vt), par, C)
+    last = path[-1]
+    k2, v2 = oracle.kv_commit(kc, vc, kt, vt, path, C)
+    n = C + L + 1
+    for h in range(nkv * grp):
+        kvh = h // grp
+        qh = torch.from_numpy(f(q[last, h])).view(1, 1, 1, hd)
+        kh = torch.from_numpy(f(k2[kvh, :n])).view(1, 1, n, hd)
+        vh = torch.from_numpy(f(v2[kvh, :n])).view(1, 1, n, hd)
+        ref = torch.nn.functional.scaled_dot_product_attention(qh, kh, vh).view(hd).numpy()
+        np.testing.assert_allclose(tree_out[last, h], ref, rtol=1e-10, atol=1e-12)
