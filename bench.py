@@ -7,8 +7,8 @@ quantized on the GPU from random-init bf16 weights, a 64-token chain-plus-branch
 tree of depth 48, KV context 2048. One measured step is one decode cycle of that
 workload: 48 draft expansion steps over the 64 tree slots (substitute stack + bf16 LM
 head + greedy top-6 child selection each), one bf16-weight target verify pass over the
-tree, row argmax of the seeded target logits and the greedy acceptance walk, with the
-accept length read back by the host.
+tree, row argmax of the seeded target logits, the greedy acceptance walk and the commit of
+the accepted tokens' K/V to the cache, with the accept length read back by the host.
 
 Printed: one JSON line. `value` is draft-tree tokens per second (48 * 64 tree tokens per
 cycle over the cycle time). The `roofline` object covers the dominant kernel, the fused
@@ -75,8 +75,10 @@ def build_model(cfg, dev, n_layers):
             w = gen.torch_normal_bf16((N, K), cfg.w_std, 0, cfg.cid, gen.TID_W, li * 16 + gen.SLOT[name], dev)
             d[name] = bq.w4_tile(*bq.quantize_substitute(w))   # the tiled layout the GEMMs stream
             t[name] = w
-        kc = gen.torch_normal_bf16((cfg.nkv, cfg.C, cfg.hd), 1.0, 0, cfg.cid, gen.TID_KC, li, dev)
-        vc = gen.torch_normal_bf16((cfg.nkv, cfg.C, cfg.hd), 1.0, 0, cfg.cid, gen.TID_VC, li, dev)
+        # C committed rows, plus room for the T rows a cycle may commit
+        pad = torch.zeros((cfg.nkv, cfg.T, cfg.hd), dtype=torch.bfloat16, device=dev)
+        kc = torch.cat([gen.torch_normal_bf16((cfg.nkv, cfg.C, cfg.hd), 1.0, 0, cfg.cid, gen.TID_KC, li, dev), pad], 1)
+        vc = torch.cat([gen.torch_normal_bf16((cfg.nkv, cfg.C, cfg.hd), 1.0, 0, cfg.cid, gen.TID_VC, li, dev), pad], 1)
         for x in (d, t):
             x.update(norm1=ones, norm2=ones, k_cache=kc, v_cache=vc)
         draft_layers.append(d)
@@ -394,10 +396,16 @@ def main():
         draft.draft_tree_step(parents, C, tk_d, tv_d, tokens=tokens, logits=logits, workspace=ws_d)
         bq.draft_select(logits, None, inv_t, TOPK, out=children)
 
+    kc_all = [ly["k_cache"] for ly in target.layers]
+    vc_all = [ly["v_cache"] for ly in target.layers]
+
     def verify():
         target.draft_tree_step(parents, C, tk_t, tv_t, tokens=tokens, logits=vlogits, workspace=ws_t)
         bq.row_argmax(seeded_logits, out=tgt)
         bq.tree_accept(parents, tokens, tgt, out=acc_out)
+        # commit the root and the accepted path's target K/V at rows C .. C + L (the next
+        # cycle would advance C by L + 1; the timed cycles keep C fixed and read rows < C)
+        bq.kv_commit(kc_all, vc_all, tk_t, tv_t, C, acc_out[0], acc_out[1])
 
     # eager reference results, then capture both phases in HIP graphs
     draft_step(); verify()
@@ -493,7 +501,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {n_layers}-layer substitute stack, T={T} tree tokens "
                                f"(chain+branches, depth 48), C={C}, vocab {V}; cycle = {DRAFT_STEPS} "
-                               f"draft steps + bf16 verify pass + argmax + greedy accept",
+                               f"draft steps + bf16 verify pass + argmax + greedy accept + KV commit",
                    "tree_tokens_per_cycle": DRAFT_STEPS * T, "accept_len": L,
                    "draft_step_ms": round(ms_draft_step, 4), "verify_ms": round(ms_verify, 4),
                    "draft_step_alg_bytes": int(step_bytes),

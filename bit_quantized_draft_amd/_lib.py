@@ -75,6 +75,9 @@ SIGNATURES = {
                                       c_void_p, c_size_t, c_void_p]),
     "ss_w4a16_gate_up_swiglu_tiled": (c_int, [c_void_p, c_int32, c_void_p, c_int64, c_int64, c_void_p,
                                               c_void_p, c_size_t, c_void_p]),
+    "ss_kv_commit": (c_int, [POINTER(c_void_p), POINTER(c_void_p), POINTER(c_void_p), POINTER(c_void_p),
+                             c_int32, c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p,
+                             c_void_p]),
     "ss_bf16_linear_workspace": (c_size_t, [c_int32, c_int64, c_int64]),
     "ss_bf16_linear": (c_int, [c_void_p, c_int32, c_void_p, c_int64, c_int64, c_void_p, c_void_p,
                                c_void_p, c_size_t, c_void_p]),

@@ -244,6 +244,19 @@ def linear_desc(entry):
     return SsLinear(kind=SS_BF16, qweight=None, scale=None, zero=None, w=entry.data_ptr())
 
 
+def kv_commit(k_caches, v_caches, tree_k, tree_v, C, path, accept_len):
+    """Copy the root's and the accepted path's tree K/V rows of every layer into the
+    caches at rows C .. C + L (path / accept_len: device outputs of tree_accept)."""
+    L = len(k_caches)
+    if not (len(v_caches) == len(tree_k) == len(tree_v) == L):
+        raise SubspecError("kv_commit: one cache and one tree K/V per layer")
+    nkv, c_stride, hd = k_caches[0].shape
+    T = tree_k[0].shape[1]
+    arr = lambda ts: (ctypes.c_void_p * L)(*[t.data_ptr() for t in ts])
+    check(lib().ss_kv_commit(arr(k_caches), arr(v_caches), arr(tree_k), arr(tree_v), L, nkv, hd, c_stride,
+                             C, T, _ptr(path), _ptr(accept_len), _stream()))
+
+
 class SubstituteModel:
     """Borrowed descriptor of a stack: per-layer weights (int4 tuples or bf16), norms, KV caches.
 
@@ -303,4 +316,4 @@ class SubstituteModel:
 __all__ = ["abi_version", "quantize_substitute", "dequantize_substitute", "w4a16_linear",
            "w4a16_gate_up_swiglu", "TiledW4", "w4_tile", "w4a16_linear_tiled", "w4a16_gate_up_swiglu_tiled",
            "bf16_linear", "tree_validate", "tree_mask", "tree_attention", "row_argmax",
-           "tree_accept", "draft_select", "SubstituteModel", "SubspecError"]
+           "tree_accept", "kv_commit", "draft_select", "SubstituteModel", "SubspecError"]

@@ -686,6 +686,43 @@ ss_status ss_tree_accept(const int32_t* parents, const int32_t* tokens, const in
   return debug_validate_parents(fn, parents, T, st);
 }
 
+ss_status ss_kv_commit(void* const* k_cache, void* const* v_cache, const void* const* k_tree,
+                       const void* const* v_tree, int32_t layers, int32_t nkv, int32_t hd, int32_t c_stride,
+                       int32_t C, int32_t T, const int32_t* path, const int32_t* accept_len, void* stream) {
+  const char* fn = __func__;
+  if (!k_cache || !v_cache || !k_tree || !v_tree)
+    return fail(SS_ERR_INVALID_ARG, "%s: the per-layer pointer arrays must be non-null", fn);
+  if (layers < 1 || nkv < 1) return fail(SS_ERR_INVALID_ARG, "%s: layers and nkv must be positive", fn);
+  if (hd != 64 && hd != 128) return fail(SS_ERR_UNSUPPORTED, "%s: hd must be 64 or 128", fn);
+  if (T < 1 || T > 256) return fail(SS_ERR_UNSUPPORTED, "%s: T must be in 1..256 (got %d)", fn, T);
+  if (C < 0 || (int64_t)C + T > c_stride)
+    return fail(SS_ERR_INVALID_ARG, "%s: need 0 <= C and C + T <= c_stride (C=%d T=%d c_stride=%d)", fn, C, T,
+                c_stride);
+  REQ_PTR(path, 4); REQ_PTR(accept_len, 4);
+  for (int l = 0; l < layers; ++l) {
+    if (!k_cache[l] || !v_cache[l] || !k_tree[l] || !v_tree[l])
+      return fail(SS_ERR_INVALID_ARG, "%s: layer %d: null cache or tree pointer", fn, l);
+    if (!aligned(k_cache[l], 16) || !aligned(v_cache[l], 16) || !aligned(k_tree[l], 16) || !aligned(v_tree[l], 16))
+      return fail(SS_ERR_INVALID_ARG, "%s: layer %d: pointers must be 16-byte aligned", fn, l);
+  }
+  ss_status s = check_device(fn);
+  if (s != SS_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int l0 = 0; l0 < layers; l0 += ss::KVC_MAX_LAYERS) {
+    const int n = std::min(layers - l0, ss::KVC_MAX_LAYERS);
+    ss::KvCommitPtrs a{};
+    for (int i = 0; i < n; ++i) {
+      a.kc[i] = static_cast<uint16_t*>(k_cache[l0 + i]);
+      a.vc[i] = static_cast<uint16_t*>(v_cache[l0 + i]);
+      a.kt[i] = static_cast<const uint16_t*>(k_tree[l0 + i]);
+      a.vt[i] = static_cast<const uint16_t*>(v_tree[l0 + i]);
+    }
+    hipError_t e = ss::launch_kv_commit(a, n, nkv, hd, c_stride, C, T, path, accept_len, st);
+    if (e != hipSuccess) return launched(fn, e, st);
+  }
+  return launched(fn, hipSuccess, st);
+}
+
 ss_status ss_draft_select(const float* logits, const float* gumbel, int32_t rows, int32_t vocab,
                           float inv_temp, int32_t k, int32_t* tokens_out, void* stream) {
   const char* fn = __func__;

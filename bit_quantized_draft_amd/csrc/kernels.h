@@ -74,6 +74,17 @@ hipError_t launch_dequantize_g64(const uint8_t* q, const uint16_t* s, const uint
 hipError_t launch_w4_tile(const uint8_t* q, const uint16_t* s, const uint16_t* z, int64_t n, int64_t k,
                           uint8_t* tiled, hipStream_t st);
 
+// KV commit: per-layer cache and tree K/V pointers (at most KVC_MAX_LAYERS per launch)
+constexpr int KVC_MAX_LAYERS = 64;
+struct KvCommitPtrs {
+  uint16_t* kc[KVC_MAX_LAYERS];
+  uint16_t* vc[KVC_MAX_LAYERS];
+  const uint16_t* kt[KVC_MAX_LAYERS];
+  const uint16_t* vt[KVC_MAX_LAYERS];
+};
+hipError_t launch_kv_commit(const KvCommitPtrs& a, int layers, int nkv, int hd, int c_stride, int C, int T,
+                            const int32_t* path, const int32_t* accept_len, hipStream_t st);
+
 // tree + attention
 hipError_t launch_tree_mask(const int32_t* parents, int T, uint64_t* mask, int32_t* depth,
                             int32_t* err, hipStream_t st);

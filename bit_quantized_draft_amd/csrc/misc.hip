@@ -278,6 +278,36 @@ hipError_t launch_qkv_rope(const SplitView& v, const float* qkv32, const int32_t
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ KV commit
+
+// Grid (layers, nkv, 2): workgroup (l, h, kv) copies the root's and the accepted path's
+// tree rows of layer l, KV head h, K (kv = 0) or V (kv = 1) to cache rows C .. C + L,
+// 16 bytes per thread and step. L comes from the device (the acceptance walk's output);
+// L and the path entries are clamped into the tree, so no access leaves the buffers.
+__global__ __launch_bounds__(256) void kv_commit_kernel(KvCommitPtrs a, int nkv, int hd, int c_stride, int C,
+                                                        int T, const int32_t* __restrict__ path,
+                                                        const int32_t* __restrict__ accept_len) {
+  const int l = blockIdx.x, h = blockIdx.y, kv = blockIdx.z;
+  const int L = min(max(*accept_len, 0), T - 1);
+  const int units = hd >> 3;   // 16-byte units per row
+  const uint16_t* src = (kv ? a.vt[l] : a.kt[l]) + (size_t)h * T * hd;
+  uint16_t* dst = (kv ? a.vc[l] : a.kc[l]) + ((size_t)h * c_stride + C) * hd;
+  for (int idx = threadIdx.x; idx < (L + 1) * units; idx += blockDim.x) {
+    const int r = idx / units, u = idx - r * units;
+    const int node = r == 0 ? 0 : min(max(path[r - 1], 0), T - 1);
+    *reinterpret_cast<u32x4_t*>(dst + (size_t)r * hd + u * 8) =
+        *reinterpret_cast<const u32x4_t*>(src + (size_t)node * hd + u * 8);
+  }
+}
+
+hipError_t launch_kv_commit(const KvCommitPtrs& a, int layers, int nkv, int hd, int c_stride, int C, int T,
+                            const int32_t* path, const int32_t* accept_len, hipStream_t st) {
+  if (layers < 1 || layers > KVC_MAX_LAYERS) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kv_commit_kernel, dim3(layers, nkv, 2), dim3(256), 0, st, a, nkv, hd, c_stride, C, T,
+                     path, accept_len);
+  return hipGetLastError();
+}
+
 hipError_t launch_embed(const int32_t* tokens, const uint16_t* embed, int T, int H, int V, float* h32,
                         int32_t* err, hipStream_t st) {
   hipLaunchKernelGGL(embed_kernel, dim3(T), dim3(256), 0, st, tokens, embed, T, H, V, h32, err);

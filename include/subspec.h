@@ -241,6 +241,23 @@ ss_status ss_tree_accept(const int32_t* parents, const int32_t* tokens,
                          int32_t* accept_len_out, int32_t* bonus_out, void* stream);
 
 /* ------------------------------------------------------------------------------
+ * KV commit after acceptance ([Review] §4.1: draft and target share one KV cache;
+ * the cycle commits the root and the L accepted nodes). Reading: for every layer and
+ * KV head, the target's tree K/V rows of the root (node 0) and of path_out[0 .. L)
+ * from ss_tree_accept, already roped at C + depth, are copied to cache rows C .. C + L
+ * in path order; nothing else is written. k_cache / v_cache: HOST arrays [layers] of
+ * bf16 [nkv][c_stride][hd]; k_tree / v_tree: HOST arrays [layers] of bf16
+ * [nkv][T][hd]; path int32 [T] and accept_len int32 [1] are DEVICE pointers (read on
+ * the device, so the call can follow ss_tree_accept inside a captured graph).
+ * L and path entries are clamped into [0, T - 1] on the device. hd in {64, 128},
+ * 1 <= T <= 256, 0 <= C, C + T <= c_stride (else SS_ERR_UNSUPPORTED / _INVALID_ARG).
+ * ------------------------------------------------------------------------------ */
+ss_status ss_kv_commit(void* const* k_cache, void* const* v_cache, const void* const* k_tree,
+                       const void* const* v_tree, int32_t layers, int32_t nkv, int32_t hd,
+                       int32_t c_stride, int32_t C, int32_t T, const int32_t* path,
+                       const int32_t* accept_len, void* stream);
+
+/* ------------------------------------------------------------------------------
  * Draft child selection with sharpening ([Summary] "Approach": draft temperature
  * 0.2; [Review] §6.3: k = 6 children). Reading: Gumbel-top-k, i.e. k tokens drawn
  * without replacement from softmax(logits / t): y = fp32(fp32(logit * inv_temp) + g),

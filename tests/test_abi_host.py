@@ -106,3 +106,13 @@ def test_workspace_queries_are_host_only(L):
 def test_attention_and_step_reject_null_arguments(L):
     assert L.ss_tree_attention(None, None, 0, None) == _lib.SS_ERR_INVALID_ARG
     assert L.ss_draft_tree_step(None, None, None, 0, None) == _lib.SS_ERR_INVALID_ARG
+
+
+def test_kv_commit_argument_checks(L):
+    arr = (ctypes.c_void_p * 1)(16)
+    dummy = ctypes.c_void_p(16)
+    # C + T beyond c_stride, unsupported hd, null arrays: rejected before any launch
+    assert L.ss_kv_commit(arr, arr, arr, arr, 1, 1, 128, 100, 90, 16, dummy, dummy, None) == _lib.SS_ERR_INVALID_ARG
+    assert b"c_stride" in L.ss_last_error()
+    assert L.ss_kv_commit(arr, arr, arr, arr, 1, 1, 96, 100, 0, 16, dummy, dummy, None) == _lib.SS_ERR_UNSUPPORTED
+    assert L.ss_kv_commit(None, arr, arr, arr, 1, 1, 128, 100, 0, 16, dummy, dummy, None) == _lib.SS_ERR_INVALID_ARG
