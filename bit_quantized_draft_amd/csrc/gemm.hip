@@ -614,9 +614,12 @@ __global__ __launch_bounds__((NWC + NLD + 1) * 64) void w4_gemm_kernel(GemmParam
 // with direct-to-LDS loads, so compute waves issue no global loads at all: a compute
 // wave never stalls at a load instruction that the busy address unit has not accepted
 // (waves issue in order, so such a stall would hold back its math). K phases: one.
-// Chunk slots (activations + weights) of the tiled kernel (about 150 KB of LDS at 64
-// tokens; deeper rings for fewer tokens measured no faster).
-constexpr int NS_T = 6;
+// Chunk slots (activations + weights) of the tiled kernel: 4 (about 100 KB of LDS at 64
+// tokens) measured faster than 2 or 6 at every token count.
+#ifndef SS_TILED_NS
+#define SS_TILED_NS 4
+#endif
+constexpr int NS_T = SS_TILED_NS;
 
 template <int TT, int EPI>
 __global__ __launch_bounds__((NWC + NLD) * 64) void w4t_gemm_kernel(GemmParams p) {
