@@ -43,7 +43,10 @@ constexpr int CHUNK_K = 128;
 #define SS_GEMM_NWC 4
 #endif
 constexpr int NWC = SS_GEMM_NWC;   // compute waves
-constexpr int NLD = 2;   // loader waves
+#ifndef SS_GEMM_NLD
+#define SS_GEMM_NLD 2
+#endif
+constexpr int NLD = SS_GEMM_NLD;   // loader waves
 constexpr int NR = 2;    // 16-row weight tiles per compute wave
 constexpr int NS = 6;    // activation chunk slots in LDS
 
@@ -627,7 +630,11 @@ __global__ __launch_bounds__((NWC + NLD) * 64) void w4t_gemm_kernel(GemmParams p
   constexpr int FRAG = TT * 4;         // 1 KB activation fragment blocks per chunk
   constexpr int NT = RG * NR;          // weight tiles per block
   constexpr int LOADS = FRAG + NT + 1; // loader instructions per chunk
-  constexpr int LA0 = 63 / LOADS < NS_T / NLD ? 63 / LOADS : NS_T / NLD;
+#ifndef SS_TILED_LA
+#define SS_TILED_LA 8
+#endif
+  constexpr int LA1 = 63 / LOADS < NS_T / NLD ? 63 / LOADS : NS_T / NLD;
+  constexpr int LA0 = LA1 < SS_TILED_LA ? LA1 : SS_TILED_LA;
   constexpr int LA = LA0 < 1 ? 1 : LA0;   // chunks in flight per loader
   static_assert(NT * 8 == 64, "one load carries the (scale, zero) words of all tiles");
   static_assert(NS_T % NLD == 0, "slot ring must split evenly");
