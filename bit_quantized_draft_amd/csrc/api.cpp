@@ -153,6 +153,7 @@ ss_status check_linear(const char* fn, const ss_linear& w, const char* name) {
 
 struct StepLayout {
   int32_t* err;
+  float* ssq;        // [T][H / 32] sums of h^2 per 32-column group (RMSNorm folded into GEMMs)
   uint64_t* mask;
   int32_t* depth;
   float* h32;
@@ -173,6 +174,7 @@ StepLayout plan_step(const ss_model* m, int T, int C, int R, void* base) {
   const int qkvN = (m->nq + 2 * m->nkv) * m->hd;
   const int rows_norm = std::max(T, R);
   L.err = bp.take<int32_t>(4);
+  L.ssq = bp.take<float>((size_t)T * (m->H / 32));
   L.mask = bp.take<uint64_t>((size_t)T * W);
   L.depth = bp.take<int32_t>(T);
   L.h32 = bp.take<float>((size_t)T * m->H);
@@ -585,15 +587,30 @@ ss_status ss_draft_tree_step(const ss_model* m, const ss_step_args* a, void* wor
     const ss_layer& ly = m->layers[l];
     uint16_t* tk = static_cast<uint16_t*>(a->tree_k[l]);
     uint16_t* tv = static_cast<uint16_t*>(a->tree_v[l]);
-    // attention block. RMSNorm-1 of layer 0 stands alone; every later RMSNorm is fused
-    // with the residual GEMM before it, which leaves its split blocks to that kernel.
-    if (l == 0)
-      RUN(ss::launch_rmsnorm(Ly.h32, static_cast<const uint16_t*>(ly.norm1), T, H, m->rms_eps, Ly.xn, nullptr, T, nullptr, st));
+    // RMSNorm is folded into the GEMM that consumes it: xn holds bf16(h * gain) and ssq the
+    // sums of h^2 per 32-column group, written by whoever finished h (row_stats for layer
+    // 0, then the residual GEMMs' epilogues and resid_finish); the consumer GEMM scales its
+    // output rows by 1 / rms.
+    if (l == 0) RUN(ss::launch_row_stats(Ly.h32, T, H, static_cast<const uint16_t*>(ly.norm1), Ly.xn, Ly.ssq, st));
+    auto consume_norm = [&](ss::GemmArgs& g) {
+      g.ssq_in = Ly.ssq;
+      g.ssq_n = H / 32;
+      g.rms_H = H;
+      g.rms_eps = m->rms_eps;
+    };
+    auto produce_norm = [&](ss::GemmArgs& g, const void* gain) {
+      if (!gain) return;
+      g.hg_out = Ly.xn;
+      g.hg_gain = static_cast<const uint16_t*>(gain);
+      g.ssq_out = Ly.ssq;
+      g.ssq_n = H / 32;
+    };
     {
       ss::GemmArgs g = gemm_args(Ly.xn, T, ly.qkv, qkvN, H);
       g.epi = ss::EPI_STORE;
       g.y_f32 = Ly.qkv32;
       g.defer_reduce = true;
+      consume_norm(g);
       const ss::GemmPlan pl = ss::plan_gemm(T, qkvN, H, g.epi, 0);
       RUN(ss::launch_gemm(g, pl, Ly.gemm_ws, st));
       RUN(ss::launch_qkv_rope(ss::gemm_split_view(pl, Ly.gemm_ws), Ly.qkv32, Ly.depth, T, C, nq, nkv, hd,
@@ -614,11 +631,12 @@ ss_status ss_draft_tree_step(const ss_model* m, const ss_step_args* a, void* wor
       g.epi = ss::EPI_RESID;
       g.resid = Ly.h32;
       g.defer_reduce = true;
+      produce_norm(g, ly.norm2);
       const ss::GemmPlan pl = ss::plan_gemm(T, H, nq * hd, g.epi, 0);
       RUN(ss::launch_gemm(g, pl, Ly.gemm_ws, st));
-      // residual add of the split blocks + RMSNorm-2
-      RUN(ss::launch_resid_norm(ss::gemm_split_view(pl, Ly.gemm_ws), Ly.h32, T, H,
-                                static_cast<const uint16_t*>(ly.norm2), m->rms_eps, Ly.xn, st));
+      // split blocks: residual add + RMSNorm-2 inputs
+      RUN(ss::launch_resid_finish(ss::gemm_split_view(pl, Ly.gemm_ws), pl.sk_blocks, Ly.h32, T, H,
+                                  static_cast<const uint16_t*>(ly.norm2), Ly.xn, Ly.ssq, st));
     }
     // MLP block
     {
@@ -626,6 +644,7 @@ ss_status ss_draft_tree_step(const ss_model* m, const ss_step_args* a, void* wor
       g.epi = ss::EPI_SWIGLU;
       g.swiglu_I = I;
       g.u_bf16 = Ly.ubuf;
+      consume_norm(g);
       RUN(ss::launch_gemm(g, ss::plan_gemm(T, 2 * I, H, g.epi, I), Ly.gemm_ws, st));
     }
     {
@@ -633,12 +652,13 @@ ss_status ss_draft_tree_step(const ss_model* m, const ss_step_args* a, void* wor
       g.epi = ss::EPI_RESID;
       g.resid = Ly.h32;
       g.defer_reduce = true;
+      // the next layer's RMSNorm-1 inputs (none after the last layer)
+      const void* next_norm = (l + 1 < m->L) ? m->layers[l + 1].norm1 : nullptr;
+      produce_norm(g, next_norm);
       const ss::GemmPlan pl = ss::plan_gemm(T, H, I, g.epi, 0);
       RUN(ss::launch_gemm(g, pl, Ly.gemm_ws, st));
-      // residual add of the split blocks + the next layer's RMSNorm-1 (none after the last)
-      const uint16_t* next_norm = (l + 1 < m->L) ? static_cast<const uint16_t*>(m->layers[l + 1].norm1) : nullptr;
-      RUN(ss::launch_resid_norm(ss::gemm_split_view(pl, Ly.gemm_ws), Ly.h32, T, H, next_norm, m->rms_eps,
-                                Ly.xn, st));
+      RUN(ss::launch_resid_finish(ss::gemm_split_view(pl, Ly.gemm_ws), pl.sk_blocks, Ly.h32, T, H,
+                                  static_cast<const uint16_t*>(next_norm), Ly.xn, Ly.ssq, st));
     }
   }
   if (a->hidden_out) RUN(ss::launch_f32_to_bf16(Ly.h32, (size_t)T * H, static_cast<uint16_t*>(a->hidden_out), st));

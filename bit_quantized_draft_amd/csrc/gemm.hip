@@ -73,6 +73,16 @@ struct GemmParams {
   int G, dp_rounds, sk_first, G_sk;
   long long sk_units;
   float* partials;     // [2 G_sk][RG][NR][TT][4][64]
+  // RMSNorm folded into the consumer: x holds bf16(h * gain); output row t is scaled by
+  // rs[t] = 1 / sqrt(sum_i ssq_in[t][i] / rms_H + rms_eps), i < ssq_n
+  const float* ssq_in;
+  int ssq_n, rms_H;
+  float rms_eps;
+  // RMSNorm inputs made by a residual GEMM (EPI_RESID): hg_out = bf16(h * hg_gain) and
+  // ssq_out[t][n / 32] = sum of h^2 over each 32-column group (ssq_n columns groups)
+  uint16_t* hg_out;
+  const uint16_t* hg_gain;
+  float* ssq_out;
 };
 
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
@@ -258,10 +268,16 @@ __device__ __forceinline__ void final_store(const GemmParams& p, const f32x4_t (
       }
     return;
   }
+  float ss[TT][4];
+#pragma unroll
+  for (int t = 0; t < TT; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ss[t][e] = 0.f;
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     if (!tile_valid<EPI, RG>(p, rb, rg, r)) continue;
     const int n = tile_row<EPI, RG>(p, rb, rg, r, j);
+    const float gn = (EPI == EPI_RESID && p.hg_out) ? bf16_to_f32(p.hg_gain[n]) : 0.f;
 #pragma unroll
     for (int t = 0; t < TT; ++t)
 #pragma unroll
@@ -271,13 +287,78 @@ __device__ __forceinline__ void final_store(const GemmParams& p, const f32x4_t (
         const size_t o = (size_t)tok * p.N + n;
         const float v = acc[r][t][e];
         if (EPI == EPI_RESID) {
-          p.resid[o] += v;
+          const float h = p.resid[o] + v;
+          p.resid[o] = h;
+          if (p.hg_out) {
+            p.hg_out[o] = f32_to_bf16(h * gn);
+            ss[t][e] += h * h;
+          }
         } else {
           if (p.y_f32) p.y_f32[o] = v;
           if (p.y_bf16) p.y_bf16[o] = f32_to_bf16(v);
         }
       }
   }
+  if (EPI == EPI_RESID && p.hg_out) {
+    // sums of squares of the wave's 32 rows (one 32-column group of the next layer's
+    // input) per token: the two tiles are in ss already, the 16 rows j across lanes
+    const int grp = (rb * RG * 32 + rg * 32) >> 5;
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x = ss[t][e];
+        x += __shfl_xor(x, 1, 16);
+        x += __shfl_xor(x, 2, 16);
+        x += __shfl_xor(x, 4, 16);
+        x += __shfl_xor(x, 8, 16);
+        const int tok = tb * 64 + t * 16 + 4 * b + e;
+        if (j == 0 && tok < p.T && rb * RG * 32 + rg * 32 < p.N) p.ssq_out[(size_t)tok * p.ssq_n + grp] = x;
+      }
+  }
+}
+
+// Row scales of RMSNorm folded into a consumer GEMM: lane l of a compute wave computes rs
+// of token tb * 64 + l into its wave's LDS row (the sums run in a fixed order: eight
+// interleaved float4 partial sums, then those in order).
+__device__ __forceinline__ void row_scales(const GemmParams& p, int tb, int lane, float* rsl) {
+  const int tok = tb * 64 + lane;
+  float r = 0.f;
+  if (tok < p.T) {
+    const float4* src = reinterpret_cast<const float4*>(p.ssq_in + (size_t)tok * p.ssq_n);
+    const int n4 = p.ssq_n >> 2;
+    float4 a[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a[k] = float4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < n4; i += 8) {
+      float4 x[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) x[k] = (i + k < n4) ? src[i + k] : float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        a[k].x += x[k].x; a[k].y += x[k].y; a[k].z += x[k].z; a[k].w += x[k].w;
+      }
+    }
+    float tot = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) tot += (a[k].x + a[k].y) + (a[k].z + a[k].w);
+    r = 1.0f / sqrtf(tot / (float)p.rms_H + p.rms_eps);
+  }
+  rsl[lane] = r;
+}
+
+// acc[r][t][e] (token t * 16 + 4 b + e of the token block) times its row scale
+template <int TT>
+__device__ __forceinline__ void apply_row_scales(f32x4_t (&acc)[NR][TT], const float* rsl, int lane) {
+  const int b = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < TT; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float sc = rsl[t * 16 + 4 * b + e];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) acc[r][t][e] *= sc;
+    }
 }
 
 // SZO: scale / zero staged per octet of chunks (8 chunks = 16 groups, 32 bytes per row
@@ -302,6 +383,7 @@ __global__ __launch_bounds__((NWC + NLD + 1) * 64) void w4_gemm_kernel(GemmParam
   __shared__ f32x4_t comb[NCB][NR][TT][64];
   __shared__ int ready[NS], done[NS];
   __shared__ int comb_ready[NCB], comb_done[NCB];
+  __shared__ float rsl[NWC][64];   // RMSNorm row scales of the current token block, per wave
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -546,10 +628,15 @@ __global__ __launch_bounds__((NWC + NLD + 1) * 64) void w4_gemm_kernel(GemmParam
       wait_eq(&oct_ready[oseq & 1], oseq);
     }
   };
+  int rs_tb = -1;
   for (int k = 0; k < nsegs; ++k) {
     int block, s0, s1;
     seg_of(p, L, g, k, block, s0, s1);
     const int len = s1 - s0;
+    if (p.ssq_in && block % p.tb_count != rs_tb) {
+      rs_tb = block % p.tb_count;
+      row_scales(p, rs_tb, lane, rsl[wave]);
+    }
     for (int p0 = 0; p0 < len; p0 += PF) {
 #pragma unroll
       for (int u = 0; u < PF; ++u) {
@@ -592,6 +679,10 @@ __global__ __launch_bounds__((NWC + NLD + 1) * 64) void w4_gemm_kernel(GemmParam
       }
     }
     if (ph == 0) {
+      if (p.ssq_in) {
+        compiler_fence();
+        apply_row_scales<TT>(acc, rsl[wave], lane);
+      }
       if (s0 == 0 && s1 == p.nsteps) {
         final_store<TT, EPI, RG>(p, acc, block, rg, lane);
       } else {
@@ -642,6 +733,7 @@ __global__ __launch_bounds__((NWC + NLD) * 64) void w4t_gemm_kernel(GemmParams p
   __shared__ u32x4_t wfrag[NS_T][NT][64];
   __shared__ uint32_t wsz[NS_T][NT * 32];
   __shared__ int ready[NS_T], done[NS_T];
+  __shared__ float rsl[NWC][64];   // RMSNorm row scales of the current token block, per wave
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -737,10 +829,14 @@ __global__ __launch_bounds__((NWC + NLD) * 64) void w4t_gemm_kernel(GemmParams p
 #pragma unroll
     for (int t = 0; t < TT; ++t) acc[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  int qs = 0;
+  int qs = 0, rs_tb = -1;
   for (int k = 0; k < nsegs; ++k) {
     int block, s0, s1;
     seg_of(p, L, g, k, block, s0, s1);
+    if (p.ssq_in && block % p.tb_count != rs_tb) {
+      rs_tb = block % p.tb_count;
+      row_scales(p, rs_tb, lane, rsl[rg]);
+    }
     for (int st = s0; st < s1; ++st, ++qs) {
       const int xs = qs % NS_T;
       wait_eq(&ready[xs], qs);
@@ -784,6 +880,11 @@ __global__ __launch_bounds__((NWC + NLD) * 64) void w4t_gemm_kernel(GemmParams p
       if (lane == 0) __hip_atomic_fetch_add(&done[xs], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     // end of segment: the result, or the partial of a block split between workgroups
+    // (partials carry the row scales too: the reduce adds scaled pieces)
+    if (p.ssq_in) {
+      compiler_fence();
+      apply_row_scales<TT>(acc, rsl[rg], lane);
+    }
     if (s0 == 0 && s1 == p.nsteps) {
       final_store<TT, EPI, RG>(p, acc, block, rg, lane);
     } else {
@@ -958,6 +1059,19 @@ hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& pl, void* ws, hipStrea
   p.G_sk = pl.G_sk;
   p.sk_units = pl.sk_units;
   p.partials = pl.sk_blocks > 0 ? reinterpret_cast<float*>(ws) : nullptr;
+  p.ssq_in = a.ssq_in;
+  p.ssq_n = a.ssq_n;
+  p.rms_H = a.rms_H;
+  p.rms_eps = a.rms_eps;
+  p.hg_out = a.hg_out;
+  p.hg_gain = a.hg_gain;
+  p.ssq_out = a.ssq_out;
+  // producers of RMSNorm inputs leave split blocks to resid_finish (deferred reduce);
+  // consumers need a 16-byte aligned sum table of whole float4s
+  if (a.hg_out && (a.epi != EPI_RESID || !a.ssq_out || !a.hg_gain || (pl.sk_blocks > 0 && !a.defer_reduce)))
+    return hipErrorInvalidValue;
+  if (a.ssq_in && ((a.ssq_n & 3) || (reinterpret_cast<uintptr_t>(a.ssq_in) & 15) || a.epi == EPI_RESID))
+    return hipErrorInvalidValue;
   const bool int4 = a.qw != nullptr;
   const bool defer = a.defer_reduce && a.epi != EPI_SWIGLU;
   // the tiled kernel has one K phase; plan_gemm's default (KS = 1) is what it needs

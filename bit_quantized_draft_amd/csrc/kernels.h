@@ -30,6 +30,16 @@ struct GemmArgs {
   uint16_t* u_bf16;
   bool defer_reduce;   // leave split blocks' partials for the consumer (see SplitView)
   bool tiled;          // qw holds the tiled layout (TILE_BLOCK_BYTES per tile and chunk)
+  // RMSNorm folded into a consumer GEMM: x = bf16(h * gain), outputs of token row t scaled
+  // by 1 / sqrt(sum(ssq_in[t][0 .. ssq_n)) / rms_H + rms_eps)
+  const float* ssq_in;
+  int ssq_n, rms_H;
+  float rms_eps;
+  // RMSNorm inputs written by an EPI_RESID GEMM for its whole blocks (split blocks: by
+  // launch_resid_finish): hg_out = bf16(h * hg_gain), ssq_out[t][n / 32] (ssq_n groups)
+  uint16_t* hg_out;
+  const uint16_t* hg_gain;
+  float* ssq_out;
 };
 
 // Decomposition of one GEMM call: row blocks x token blocks, each cut into steps of KS
@@ -58,8 +68,10 @@ SplitView gemm_split_view(const GemmPlan& pl, const void* ws);
 // Finish a deferred residual GEMM and normalize: for every token row t, h32[t] += the
 // split blocks' sums, then xn[t] = bf16(h32[t] * rsqrt(mean(h32[t]^2) + eps) * gain) when
 // gain is not null. H <= 8192.
-hipError_t launch_resid_norm(const SplitView& v, float* h32, int T, int H, const uint16_t* gain,
-                             float eps, uint16_t* xn, hipStream_t st);
+hipError_t launch_resid_finish(const SplitView& v, int sk_blocks, float* h32, int T, int H,
+                               const uint16_t* gain, uint16_t* hg, float* ssq, hipStream_t st);
+hipError_t launch_row_stats(const float* h32, int T, int H, const uint16_t* gain, uint16_t* hg, float* ssq,
+                            hipStream_t st);
 // Finish a deferred qkv GEMM (values of unsplit blocks are read from qkv32) and apply
 // RoPE + the q / tree-K / tree-V scatter of launch_rope_split.
 hipError_t launch_qkv_rope(const SplitView& v, const float* qkv32, const int32_t* depth, int T, int C,

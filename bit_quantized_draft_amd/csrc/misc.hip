@@ -136,48 +136,83 @@ constexpr int SV_THREADS = 256;      // qkv split finish: threads per part of a 
 constexpr int SV_PARTS = 4;          // qkv split finish: parts (head ranges) per row
 constexpr int SV_MAX_BLOCKS = 128;   // row blocks per token row
 constexpr int SV_MAX_PART = SV_THREADS * 8;   // columns per part (the largest KM is 8)
-constexpr int RN_THREADS = 1024;     // residual split finish + RMSNorm: one workgroup per row
-constexpr int RN_MAX_W = RN_THREADS * 8;
-
-// One workgroup per token row: finish the split blocks of a residual GEMM into h32[t]
-// (h += sum of pieces; blocks the GEMM stored itself are already in h32), then, when gain
-// is given, the row's RMSNorm into xn. (Spreading a row over several workgroups needs a
-// device-scope hand-off for the norm; its fences cost more than the row's loads.)
-template <int KM>
-__global__ __launch_bounds__(RN_THREADS) void resid_norm_kernel(SplitView v, float* __restrict__ h32, int H,
-                                                                const uint16_t* __restrict__ gain, float eps,
-                                                                uint16_t* __restrict__ xn) {
-  __shared__ SvBlock blk[SV_MAX_BLOCKS];
-  __shared__ float red[RN_THREADS / 64];
-  const int t = blockIdx.x, tb = t >> 6;
-  for (int rb = threadIdx.x; rb < v.rb_count; rb += blockDim.x) blk[rb] = sv_block(v, tb + rb * v.tb_count);
-  __syncthreads();
-  float* row = h32 + (size_t)t * H;
-  float hv[KM];
-  sv_row<KM>(v, blk, t, 0, H, row, true, hv);
+// Residual GEMM, split blocks: workgroup (sb, rg, tt) finishes the 32 rows of row group
+// rg of split block sk_first + sb for the 16 tokens of token tile tt (512 elements, two
+// per thread): h += the pieces' partials in K order, h32 updated and, with a gain, the
+// next RMSNorm's inputs: hg = bf16(h * gain) and ssq[t][n / 32], the group's sum of h^2
+// (the 16 rows j across lanes, the two tiles in each thread). Blocks the GEMM finished
+// itself (one owner) are skipped: their epilogue wrote the same outputs.
+template <int TT>
+__global__ __launch_bounds__(256) void resid_finish_kernel(SplitView v, float* __restrict__ h32, int T, int H,
+                                                           const uint16_t* __restrict__ gain,
+                                                           uint16_t* __restrict__ hg, float* __restrict__ ssq) {
+  const int sb = blockIdx.x, rg = blockIdx.y, tt = blockIdx.z;
+  const int b = v.sk_first + sb;
+  const SvBlock blk = sv_block(v, b);
+  if (blk.g0 == blk.g1) return;
+  const int tb = b % v.tb_count, rb = b / v.tb_count;
+  const int lane = threadIdx.x & 63, e = threadIdx.x >> 6;
+  const int j = lane & 15, bq = lane >> 4;
+  const int tok = tb * 64 + tt * 16 + 4 * bq + e;
+  const size_t se = (size_t)v.RG * 2 * v.TT * 256;   // floats per partial slot
+  const int np = blk.g1 - blk.g0 + 1;
   float ss = 0.f;
 #pragma unroll
-  for (int k = 0; k < KM; ++k) {
-    const int n = k * RN_THREADS + threadIdx.x;
-    if (n < H) {
-      const SvBlock b = blk[n / v.rows_per_block];
-      if (b.g1 != b.g0) row[n] = hv[k];
-      ss += hv[k] * hv[k];
+  for (int r = 0; r < 2; ++r) {
+    const int n = rb * v.rows_per_block + rg * 32 + r * 16 + j;
+    const size_t off = (size_t)rg * (2 * v.TT * 256) + ((r * v.TT + tt) * 4 + e) * 64 + 16 * bq + j;
+    float sum = 0.f;
+    for (int p0 = 0; p0 < np; p0 += 8) {   // eight independent loads in flight, added in order
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int pi = p0 + i;
+        const size_t slot = pi == 0 ? (size_t)blk.slot0 : (size_t)(2 * (blk.g0 + pi));
+        x[i] = pi < np ? v.partials[slot * se + off] : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (p0 + i < np) sum += x[i];
+    }
+    if (tok < T && n < H) {
+      const size_t o = (size_t)tok * H + n;
+      const float h = h32[o] + sum;
+      h32[o] = h;
+      if (gain) {
+        hg[o] = f32_to_bf16(h * bf16_to_f32(gain[n]));
+        ss += h * h;
+      }
     }
   }
   if (!gain) return;
-  ss = wave_sum(ss);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  float tot = 0.f;
-#pragma unroll
-  for (int w = 0; w < RN_THREADS / 64; ++w) tot += red[w];
-  const float rs = 1.0f / sqrtf(tot / (float)H + eps);
-  uint16_t* o = xn + (size_t)t * H;
-#pragma unroll
-  for (int k = 0; k < KM; ++k) {
-    const int n = k * RN_THREADS + threadIdx.x;
-    if (n < H) o[n] = f32_to_bf16(hv[k] * rs * bf16_to_f32(gain[n]));
+  ss += __shfl_xor(ss, 1, 16);
+  ss += __shfl_xor(ss, 2, 16);
+  ss += __shfl_xor(ss, 4, 16);
+  ss += __shfl_xor(ss, 8, 16);
+  const int grp = (rb * v.rows_per_block + rg * 32) >> 5;
+  if (j == 0 && tok < T && grp * 32 < H) ssq[(size_t)tok * (H >> 5) + grp] = ss;
+}
+
+// The first RMSNorm's inputs from h32 (one workgroup per token row): hg = bf16(h * gain)
+// and ssq[t][n / 32], each 32-column group's sum of h^2 (32 lanes, fixed order).
+__global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict__ h32, int H,
+                                                        const uint16_t* __restrict__ gain,
+                                                        uint16_t* __restrict__ hg, float* __restrict__ ssq) {
+  const int t = blockIdx.x;
+  for (int n0 = 0; n0 < H; n0 += blockDim.x) {
+    const int n = n0 + threadIdx.x;
+    float x = 0.f;
+    if (n < H) {
+      const float h = h32[(size_t)t * H + n];
+      hg[(size_t)t * H + n] = f32_to_bf16(h * bf16_to_f32(gain[n]));
+      x = h * h;
+    }
+    x += __shfl_xor(x, 1, 32);
+    x += __shfl_xor(x, 2, 32);
+    x += __shfl_xor(x, 4, 32);
+    x += __shfl_xor(x, 8, 32);
+    x += __shfl_xor(x, 16, 32);
+    if ((threadIdx.x & 31) == 0 && n < H) ssq[(size_t)t * (H >> 5) + (n >> 5)] = x;
   }
 }
 
@@ -247,17 +282,25 @@ bool sv_fits(const SplitView& v) {
 }
 }  // namespace
 
-hipError_t launch_resid_norm(const SplitView& v, float* h32, int T, int H, const uint16_t* gain,
-                             float eps, uint16_t* xn, hipStream_t st) {
-  if (H > RN_MAX_W || v.rb_count > SV_MAX_BLOCKS || !sv_fits(v)) return hipErrorInvalidValue;
-  const int need = (H + RN_THREADS - 1) / RN_THREADS;
-  const int km = need <= 2 ? 2 : need <= 4 ? 4 : need <= 6 ? 6 : 8;
-  switch (km) {
-    case 2: hipLaunchKernelGGL(resid_norm_kernel<2>, dim3(T), dim3(RN_THREADS), 0, st, v, h32, H, gain, eps, xn); break;
-    case 4: hipLaunchKernelGGL(resid_norm_kernel<4>, dim3(T), dim3(RN_THREADS), 0, st, v, h32, H, gain, eps, xn); break;
-    case 6: hipLaunchKernelGGL(resid_norm_kernel<6>, dim3(T), dim3(RN_THREADS), 0, st, v, h32, H, gain, eps, xn); break;
-    default: hipLaunchKernelGGL(resid_norm_kernel<8>, dim3(T), dim3(RN_THREADS), 0, st, v, h32, H, gain, eps, xn); break;
+hipError_t launch_resid_finish(const SplitView& v, int sk_blocks, float* h32, int T, int H,
+                               const uint16_t* gain, uint16_t* hg, float* ssq, hipStream_t st) {
+  if (sk_blocks == 0) return hipSuccess;
+  if (!sv_fits(v) || v.rows_per_block != v.RG * 32 || (H & 31) || (gain && (!hg || !ssq)))
+    return hipErrorInvalidValue;
+  const dim3 grid(sk_blocks, v.RG, v.TT);
+  switch (v.TT) {
+    case 1: hipLaunchKernelGGL(resid_finish_kernel<1>, grid, dim3(256), 0, st, v, h32, T, H, gain, hg, ssq); break;
+    case 2: hipLaunchKernelGGL(resid_finish_kernel<2>, grid, dim3(256), 0, st, v, h32, T, H, gain, hg, ssq); break;
+    case 3: hipLaunchKernelGGL(resid_finish_kernel<3>, grid, dim3(256), 0, st, v, h32, T, H, gain, hg, ssq); break;
+    default: hipLaunchKernelGGL(resid_finish_kernel<4>, grid, dim3(256), 0, st, v, h32, T, H, gain, hg, ssq); break;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_row_stats(const float* h32, int T, int H, const uint16_t* gain, uint16_t* hg, float* ssq,
+                            hipStream_t st) {
+  if (H & 31) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(row_stats_kernel, dim3(T), dim3(256), 0, st, h32, H, gain, hg, ssq);
   return hipGetLastError();
 }
 
