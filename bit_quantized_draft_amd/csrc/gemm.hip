@@ -318,33 +318,43 @@ __device__ __forceinline__ void final_store(const GemmParams& p, const f32x4_t (
   }
 }
 
-// Row scales of RMSNorm folded into a consumer GEMM: lane l of a compute wave computes rs
-// of token tb * 64 + l into its wave's LDS row (the sums run in a fixed order: eight
-// interleaved float4 partial sums, then those in order).
-__device__ __forceinline__ void row_scales(const GemmParams& p, int tb, int lane, float* rsl) {
-  const int tok = tb * 64 + lane;
-  float r = 0.f;
-  if (tok < p.T) {
-    const float4* src = reinterpret_cast<const float4*>(p.ssq_in + (size_t)tok * p.ssq_n);
-    const int n4 = p.ssq_n >> 2;
-    float4 a[8];
+// Row scales of RMSNorm folded into a consumer GEMM, for all T tokens, computed once per
+// workgroup by its nw compute waves together: wave w takes tokens [w per, (w + 1) per),
+// lpt lanes per token each add a strided share of the token's partial sums (eight float4
+// loads in flight), the lpt shares are combined by an xor tree (a fixed order), and the
+// result goes to rs_all in LDS; each wave then counts itself in rs_done.
+__device__ __forceinline__ void row_scales(const GemmParams& p, int wave, int nw, int lane, float* rs_all,
+                                           int* rs_done) {
+  const int per = (p.T + nw - 1) / nw;
+  int lpt = 64;
+  while (lpt > 1 && lpt * per > 64) lpt >>= 1;   // lanes per token
+  const int tpw = 64 / lpt;                       // tokens per pass
+  const int n4 = p.ssq_n >> 2;
+  const int part = lane % lpt;
+  for (int base = 0; base < per; base += tpw) {   // uniform trip count
+    const int tl = base + lane / lpt;
+    const int tok = wave * per + tl;
+    const bool ok = tl < per && tok < p.T;
+    float s = 0.f;
+    if (ok) {
+      const float4* src = reinterpret_cast<const float4*>(p.ssq_in + (size_t)tok * p.ssq_n);
+      for (int i0 = part; i0 < n4; i0 += 8 * lpt) {
+        float4 x[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) a[k] = float4{0.f, 0.f, 0.f, 0.f};
-    for (int i = 0; i < n4; i += 8) {
-      float4 x[8];
+        for (int k = 0; k < 8; ++k) {
+          const int i = i0 + k * lpt;
+          x[k] = i < n4 ? src[i] : float4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
-      for (int k = 0; k < 8; ++k) x[k] = (i + k < n4) ? src[i + k] : float4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        a[k].x += x[k].x; a[k].y += x[k].y; a[k].z += x[k].z; a[k].w += x[k].w;
+        for (int k = 0; k < 8; ++k) s += (x[k].x + x[k].y) + (x[k].z + x[k].w);
       }
     }
-    float tot = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) tot += (a[k].x + a[k].y) + (a[k].z + a[k].w);
-    r = 1.0f / sqrtf(tot / (float)p.rms_H + p.rms_eps);
+    for (int o = 1; o < lpt; o <<= 1) s += __shfl_xor(s, o, 64);
+    if (ok && part == 0) rs_all[tok] = 1.0f / sqrtf(s / (float)p.rms_H + p.rms_eps);
   }
-  rsl[lane] = r;
+  compiler_fence();
+  lds_wait();
+  if (lane == 0) __hip_atomic_fetch_add(rs_done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 // acc[r][t][e] (token t * 16 + 4 b + e of the token block) times its row scale
@@ -383,7 +393,8 @@ __global__ __launch_bounds__((NWC + NLD + 1) * 64) void w4_gemm_kernel(GemmParam
   __shared__ f32x4_t comb[NCB][NR][TT][64];
   __shared__ int ready[NS], done[NS];
   __shared__ int comb_ready[NCB], comb_done[NCB];
-  __shared__ float rsl[NWC][64];   // RMSNorm row scales of the current token block, per wave
+  __shared__ float rs_all[256];    // RMSNorm row scales of all tokens (consumer GEMMs)
+  __shared__ int rs_done;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -404,6 +415,8 @@ __global__ __launch_bounds__((NWC + NLD + 1) * 64) void w4_gemm_kernel(GemmParam
     oct_ready[tid] = -1;
     oct_done[tid] = 0;
   }
+  if (tid < 256) rs_all[tid] = 0.f;
+  if (tid == 0) rs_done = 0;
   __syncthreads();   // the only workgroup barrier
 
   if (SZO && wave == NWC + NLD) {
@@ -628,15 +641,12 @@ __global__ __launch_bounds__((NWC + NLD + 1) * 64) void w4_gemm_kernel(GemmParam
       wait_eq(&oct_ready[oseq & 1], oseq);
     }
   };
-  int rs_tb = -1;
+  if (p.ssq_in) row_scales(p, wave, NWC, lane, rs_all, &rs_done);
+  bool rs_seen = false;
   for (int k = 0; k < nsegs; ++k) {
     int block, s0, s1;
     seg_of(p, L, g, k, block, s0, s1);
     const int len = s1 - s0;
-    if (p.ssq_in && block % p.tb_count != rs_tb) {
-      rs_tb = block % p.tb_count;
-      row_scales(p, rs_tb, lane, rsl[wave]);
-    }
     for (int p0 = 0; p0 < len; p0 += PF) {
 #pragma unroll
       for (int u = 0; u < PF; ++u) {
@@ -680,8 +690,11 @@ __global__ __launch_bounds__((NWC + NLD + 1) * 64) void w4_gemm_kernel(GemmParam
     }
     if (ph == 0) {
       if (p.ssq_in) {
-        compiler_fence();
-        apply_row_scales<TT>(acc, rsl[wave], lane);
+        if (!rs_seen) {
+          wait_ge(&rs_done, NWC);
+          rs_seen = true;
+        }
+        apply_row_scales<TT>(acc, rs_all + (block % p.tb_count) * 64, lane);
       }
       if (s0 == 0 && s1 == p.nsteps) {
         final_store<TT, EPI, RG>(p, acc, block, rg, lane);
@@ -733,7 +746,8 @@ __global__ __launch_bounds__((NWC + NLD) * 64) void w4t_gemm_kernel(GemmParams p
   __shared__ u32x4_t wfrag[NS_T][NT][64];
   __shared__ uint32_t wsz[NS_T][NT * 32];
   __shared__ int ready[NS_T], done[NS_T];
-  __shared__ float rsl[NWC][64];   // RMSNorm row scales of the current token block, per wave
+  __shared__ float rs_all[256];    // RMSNorm row scales of all tokens (consumer GEMMs)
+  __shared__ int rs_done;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -746,6 +760,8 @@ __global__ __launch_bounds__((NWC + NLD) * 64) void w4t_gemm_kernel(GemmParams p
     ready[tid] = -1;
     done[tid] = 0;
   }
+  if (tid < 256) rs_all[tid] = 0.f;
+  if (tid == 0) rs_done = 0;
   __syncthreads();   // the only workgroup barrier
 
   if (wave >= NWC) {
@@ -829,14 +845,12 @@ __global__ __launch_bounds__((NWC + NLD) * 64) void w4t_gemm_kernel(GemmParams p
 #pragma unroll
     for (int t = 0; t < TT; ++t) acc[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  int qs = 0, rs_tb = -1;
+  if (p.ssq_in) row_scales(p, rg, NWC, lane, rs_all, &rs_done);
+  bool rs_seen = false;
+  int qs = 0;
   for (int k = 0; k < nsegs; ++k) {
     int block, s0, s1;
     seg_of(p, L, g, k, block, s0, s1);
-    if (p.ssq_in && block % p.tb_count != rs_tb) {
-      rs_tb = block % p.tb_count;
-      row_scales(p, rs_tb, lane, rsl[rg]);
-    }
     for (int st = s0; st < s1; ++st, ++qs) {
       const int xs = qs % NS_T;
       wait_eq(&ready[xs], qs);
@@ -882,8 +896,11 @@ __global__ __launch_bounds__((NWC + NLD) * 64) void w4t_gemm_kernel(GemmParams p
     // end of segment: the result, or the partial of a block split between workgroups
     // (partials carry the row scales too: the reduce adds scaled pieces)
     if (p.ssq_in) {
-      compiler_fence();
-      apply_row_scales<TT>(acc, rsl[rg], lane);
+      if (!rs_seen) {
+        wait_ge(&rs_done, NWC);
+        rs_seen = true;
+      }
+      apply_row_scales<TT>(acc, rs_all + (block % p.tb_count) * 64, lane);
     }
     if (s0 == 0 && s1 == p.nsteps) {
       final_store<TT, EPI, RG>(p, acc, block, rg, lane);
