@@ -156,6 +156,7 @@ struct StepLayout {
   float* ssq;        // [T][H / 32] sums of h^2 per 32-column group (RMSNorm folded into GEMMs)
   uint64_t* mask;
   int32_t* depth;
+  float2* rope;      // [T][hd / 2] (cos, sin) of the step's RoPE angles
   float* h32;
   uint16_t* xn;
   float* qkv32;
@@ -177,6 +178,7 @@ StepLayout plan_step(const ss_model* m, int T, int C, int R, void* base) {
   L.ssq = bp.take<float>((size_t)T * (m->H / 32));
   L.mask = bp.take<uint64_t>((size_t)T * W);
   L.depth = bp.take<int32_t>(T);
+  L.rope = bp.take<float2>((size_t)T * (m->hd / 2));
   L.h32 = bp.take<float>((size_t)T * m->H);
   L.xn = bp.take<uint16_t>((size_t)rows_norm * m->H);
   L.qkv32 = bp.take<float>((size_t)T * qkvN);
@@ -579,6 +581,7 @@ ss_status ss_draft_tree_step(const ss_model* m, const ss_step_args* a, void* wor
   } while (0)
 
   RUN(ss::launch_tree_mask(a->parents, T, Ly.mask, Ly.depth, Ly.err, st));
+  RUN(ss::launch_rope_table(Ly.depth, T, C, hd, m->rope_theta, Ly.rope, st));
   if (a->hidden_in) RUN(ss::launch_bf16_to_f32(static_cast<const uint16_t*>(a->hidden_in), (size_t)T * H, Ly.h32, st));
   else RUN(ss::launch_embed(a->tokens, static_cast<const uint16_t*>(m->embed), T, H, m->V, Ly.h32, Ly.err, st));
 
@@ -613,8 +616,8 @@ ss_status ss_draft_tree_step(const ss_model* m, const ss_step_args* a, void* wor
       consume_norm(g);
       const ss::GemmPlan pl = ss::plan_gemm(T, qkvN, H, g.epi, 0);
       RUN(ss::launch_gemm(g, pl, Ly.gemm_ws, st));
-      RUN(ss::launch_qkv_rope(ss::gemm_split_view(pl, Ly.gemm_ws), Ly.qkv32, Ly.depth, T, C, nq, nkv, hd,
-                              m->rope_theta, Ly.qbuf, tk, tv, st));
+      RUN(ss::launch_qkv_finish(ss::gemm_split_view(pl, Ly.gemm_ws), Ly.qkv32, Ly.rope, T, nq, nkv, hd,
+                                Ly.qbuf, tk, tv, st));
     }
     {
       ss::AttnArgs aa{};

@@ -72,11 +72,15 @@ hipError_t launch_resid_finish(const SplitView& v, int sk_blocks, float* h32, in
                                const uint16_t* gain, uint16_t* hg, float* ssq, hipStream_t st);
 hipError_t launch_row_stats(const float* h32, int T, int H, const uint16_t* gain, uint16_t* hg, float* ssq,
                             hipStream_t st);
-// Finish a deferred qkv GEMM (values of unsplit blocks are read from qkv32) and apply
-// RoPE + the q / tree-K / tree-V scatter of launch_rope_split.
-hipError_t launch_qkv_rope(const SplitView& v, const float* qkv32, const int32_t* depth, int T, int C,
-                           int nq, int nkv, int hd, float theta, uint16_t* q, uint16_t* kt,
-                           uint16_t* vt, hipStream_t st);
+// RoPE angles of one step: rope[t][i] = (cos, sin) of (C + depth[t]) theta^(-2i/hd) for
+// i < hd/2, evaluated in fp64 and rounded to fp32 (all layers share them).
+hipError_t launch_rope_table(const int32_t* depth, int T, int C, int hd, float theta, float2* rope,
+                             hipStream_t st);
+// Finish a deferred qkv GEMM (values of unsplit blocks are read from qkv32), apply RoPE
+// from the step's table to the q and k heads and scatter to q [T][nq][hd] and tree K / V
+// [nkv][T][hd] (bf16).
+hipError_t launch_qkv_finish(const SplitView& v, const float* qkv32, const float2* rope, int T, int nq, int nkv,
+                             int hd, uint16_t* q, uint16_t* kt, uint16_t* vt, hipStream_t st);
 
 // quantization
 hipError_t launch_quantize_g64(const uint16_t* w, int64_t n, int64_t k, uint8_t* q, uint16_t* s,
@@ -131,9 +135,6 @@ hipError_t launch_f32_to_bf16(const float* in, size_t n, uint16_t* out, hipStrea
 hipError_t launch_rmsnorm(const float* h32, const uint16_t* gain, int R, int H, float eps,
                           uint16_t* out, const int32_t* rows, int src_rows, int32_t* err,
                           hipStream_t st);
-hipError_t launch_rope_split(const float* qkv, const int32_t* depth, int T, int C, int nq, int nkv,
-                             int hd, float theta, uint16_t* q, uint16_t* kt, uint16_t* vt,
-                             hipStream_t st);
 
 // selection / acceptance
 hipError_t launch_row_argmax(const float* logits, int rows, int vocab, int32_t* out, hipStream_t st);

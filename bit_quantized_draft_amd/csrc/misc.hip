@@ -92,50 +92,9 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   for (int i = RMS_CACHE * 256 + threadIdx.x; i < H4; i += 256) emit(i, x4[i]);
 }
 
-// qkv fp32 [T][(nq+2nkv)*hd] -> q bf16 [T][nq][hd] and tree K/V bf16 [nkv][T][hd].
-// RoPE (rotate-half) on q and k at position C + depth[t]; angles in fp64.
-__global__ __launch_bounds__(256) void rope_split_kernel(const float* __restrict__ qkv,
-                                                         const int32_t* __restrict__ depth, int T,
-                                                         int C, int nq, int nkv, int hd,
-                                                         double theta, uint16_t* __restrict__ q,
-                                                         uint16_t* __restrict__ kt,
-                                                         uint16_t* __restrict__ vt) {
-  __shared__ float cs[64], sn[64];   // hd <= 128
-  const int t = blockIdx.x;
-  const int half = hd >> 1;
-  const int width = (nq + 2 * nkv) * hd;
-  const double pos = (double)(C + depth[t]);
-  if (threadIdx.x < half) {
-    const double inv = pow(theta, -2.0 * (double)threadIdx.x / (double)hd);
-    double sd, cd;
-    sincos(pos * inv, &sd, &cd);
-    cs[threadIdx.x] = (float)cd;
-    sn[threadIdx.x] = (float)sd;
-  }
-  __syncthreads();
-  const float* row = qkv + (size_t)t * width;
-  for (int e = threadIdx.x; e < (nq + nkv) * half; e += blockDim.x) {
-    const int h = e / half, i = e - h * half;
-    const float c = cs[i], s = sn[i];
-    const float a = row[h * hd + i], bb = row[h * hd + i + half];
-    const float r0 = a * c - bb * s;
-    const float r1 = bb * c + a * s;
-    uint16_t* dst = (h < nq) ? q + ((size_t)t * nq + h) * hd : kt + ((size_t)(h - nq) * T + t) * hd;
-    dst[i] = f32_to_bf16(r0);
-    dst[i + half] = f32_to_bf16(r1);
-  }
-  for (int i = threadIdx.x; i < nkv * hd; i += blockDim.x) {
-    const int kh = i / hd, d = i % hd;
-    vt[((size_t)kh * T + t) * hd + d] = f32_to_bf16(row[(nq + nkv) * hd + i]);
-  }
-}
 
 // ------------------------------------------------------------------ fused split finish
 
-constexpr int SV_THREADS = 256;      // qkv split finish: threads per part of a row
-constexpr int SV_PARTS = 4;          // qkv split finish: parts (head ranges) per row
-constexpr int SV_MAX_BLOCKS = 128;   // row blocks per token row
-constexpr int SV_MAX_PART = SV_THREADS * 8;   // columns per part (the largest KM is 8)
 // Residual GEMM, split blocks: workgroup (sb, rg, tt) finishes the 32 rows of row group
 // rg of split block sk_first + sb for the 16 tokens of token tile tt (512 elements, two
 // per thread): h += the pieces' partials in K order, h32 updated and, with a gain, the
@@ -216,66 +175,86 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict_
   }
 }
 
-// Workgroup (t, part) finishes the split qkv blocks of heads [h0, h1) of row t into LDS,
-// then applies RoPE (rotate-half) to its q and k heads at position C + depth[t] with fp64
-// angles and scatters to q [T][nq][hd] and tree K / V [nkv][T][hd] (bf16). RoPE stays
-// inside a head, so the parts are independent.
-template <int KM>
-__global__ __launch_bounds__(SV_THREADS) void qkv_rope_kernel(SplitView v, const float* __restrict__ qkv,
-                                                              const int32_t* __restrict__ depth, int T, int C,
-                                                              int nq, int nkv, int hd, double theta,
-                                                              uint16_t* __restrict__ q, uint16_t* __restrict__ kt,
-                                                              uint16_t* __restrict__ vt) {
-  __shared__ SvBlock blk[SV_MAX_BLOCKS];
-  __shared__ float rowv[SV_MAX_PART];
-  __shared__ float cs[64], sn[64];   // hd <= 128
-  const int t = blockIdx.x, part = blockIdx.y, tb = t >> 6;
-  const int half = hd >> 1;
-  const int NH = nq + 2 * nkv;
-  const int h0 = part * NH / SV_PARTS, h1 = (part + 1) * NH / SV_PARTS;
-  const int W = NH * hd;
-  const int c0 = h0 * hd, c1 = h1 * hd;
-  for (int rb = threadIdx.x; rb < v.rb_count; rb += blockDim.x) blk[rb] = sv_block(v, tb + rb * v.tb_count);
-  if (threadIdx.x < half) {
-    const double pos = (double)(C + depth[t]);
-    const double inv = pow(theta, -2.0 * (double)threadIdx.x / (double)hd);
-    double sd, cd;
-    sincos(pos * inv, &sd, &cd);
-    cs[threadIdx.x] = (float)cd;
-    sn[threadIdx.x] = (float)sd;
-  }
-  __syncthreads();
-  float val[KM];
-  sv_row<KM>(v, blk, t, c0, c1, qkv + (size_t)t * W, false, val);
+// RoPE table of a step (every layer uses the same positions): rope[t][i] = (cos, sin) of
+// (C + depth[t]) * theta^(-2i/hd), angles in fp64, rounded to fp32 once.
+__global__ __launch_bounds__(64) void rope_table_kernel(const int32_t* __restrict__ depth, int C, int hd,
+                                                        double theta, float2* __restrict__ rope) {
+  const int t = blockIdx.x, i = threadIdx.x, half = hd >> 1;
+  if (i >= half) return;
+  const double pos = (double)(C + depth[t]);
+  const double inv = pow(theta, -2.0 * (double)i / (double)hd);
+  double sd, cd;
+  sincos(pos * inv, &sd, &cd);
+  rope[(size_t)t * half + i] = float2{(float)cd, (float)sd};
+}
+
+// qkv GEMM output -> q bf16 [T][nq][hd] and tree K / V bf16 [nkv][T][hd], element-parallel.
+// Workgroup (c, pp, tt) takes one RoPE pair of 16-row sub-tiles of the 128-row chunk c
+// (a head spans ds = hd / 16 sub-tiles; row i of a head pairs with row i + hd/2, ds / 2
+// sub-tiles on) for the 16 tokens of token tile tt; thread (e, bq, j) holds row j of both
+// sub-tiles for token 16 tt + 4 bq + e, the GEMM's fragment order, so a wave reads 256
+// contiguous bytes of a partial slot per sub-tile and piece. Which block a sub-tile lies
+// in, its pieces and their slots are the same for the whole workgroup (scalar registers);
+// a split block's value is its pieces' partials summed in K order, any other value is
+// read from qkv32.
+__device__ __forceinline__ float qkv_value(const SplitView& v, const float* __restrict__ qkv32, int W, int tt,
+                                           int n0, int lane_off, int tok, int j) {
+  const SvBlock b = sv_block(v, (tt >> 2) + (n0 / v.rows_per_block) * v.tb_count);
+  if (b.g1 == b.g0) return qkv32[(size_t)tok * W + n0 + j];
+  const int np = b.g1 - b.g0 + 1;
+  const int nn = n0 % v.rows_per_block;
+  const size_t se = (size_t)v.RG * 2 * v.TT * 256;   // floats per partial slot
+  const float* base = v.partials + (nn >> 5) * (2 * v.TT * 256) + ((((nn >> 4) & 1) * v.TT + (tt & 3)) * 4) * 64;
+  float x = 0.f;
+  for (int p0 = 0; p0 < np; p0 += SV_BATCH) {   // independent loads in flight, added in order
+    float y[SV_BATCH];
 #pragma unroll
-  for (int k = 0; k < KM; ++k) {
-    const int n = c0 + k * SV_THREADS + threadIdx.x;
-    if (n < c1) rowv[n - c0] = val[k];
+    for (int i = 0; i < SV_BATCH; ++i) {
+      const int pi = p0 + i;
+      const size_t slot = pi == 0 ? (size_t)b.slot0 : (size_t)(2 * (b.g0 + pi));
+      y[i] = pi < np ? base[slot * se + lane_off] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < SV_BATCH; ++i)
+      if (p0 + i < np) x += y[i];
   }
-  __syncthreads();
-  const int hr = min(h1, nq + nkv);   // rotated heads of this part: [h0, hr)
-  for (int e = threadIdx.x; e < (hr - h0) * half; e += blockDim.x) {
-    const int h = h0 + e / half, i = e % half;
-    const float c = cs[i], s = sn[i];
-    const float a = rowv[(h - h0) * hd + i], bb = rowv[(h - h0) * hd + i + half];
-    const float r0 = a * c - bb * s;
-    const float r1 = bb * c + a * s;
-    uint16_t* dst = (h < nq) ? q + ((size_t)t * nq + h) * hd : kt + ((size_t)(h - nq) * T + t) * hd;
-    dst[i] = f32_to_bf16(r0);
-    dst[i + half] = f32_to_bf16(r1);
+  return x;
+}
+
+__global__ __launch_bounds__(256) void qkv_finish_kernel(SplitView v, const float* __restrict__ qkv32,
+                                                         const float2* __restrict__ rope, int T, int nq, int nkv,
+                                                         int hd, uint16_t* __restrict__ q, uint16_t* __restrict__ kt,
+                                                         uint16_t* __restrict__ vt) {
+  const int c = blockIdx.x >> 2, pp = blockIdx.x & 3, tt = blockIdx.y;
+  const int W = (nq + 2 * nkv) * hd;
+  const int ds = hd >> 4, hs = ds >> 1;
+  const int s0 = (pp / hs) * ds + pp % hs;   // first sub-tile of the pair; its partner is s0 + hs
+  const int n0 = c * 128 + s0 * 16;          // first row of the first sub-tile
+  if (n0 >= W) return;
+  const int lane = threadIdx.x & 63, e = threadIdx.x >> 6;
+  const int j = lane & 15, bq = lane >> 4;
+  const int tok = tt * 16 + 4 * bq + e;
+  if (tok >= T) return;
+  const int lane_off = e * 64 + 16 * bq + j;
+  const int h = n0 / hd, i = n0 - h * hd + j;
+  const int half = hd >> 1;
+  const bool rot = h < nq + nkv;
+  float2 cs{1.f, 0.f};
+  if (rot) cs = rope[(size_t)tok * half + i];
+  const float a = qkv_value(v, qkv32, W, tt, n0, lane_off, tok, j);
+  const float bb = qkv_value(v, qkv32, W, tt, n0 + half, lane_off, tok, j);
+  if (!rot) {   // value head: no rotation
+    uint16_t* dst = vt + ((size_t)(h - nq - nkv) * T + tok) * hd;
+    dst[i] = f32_to_bf16(a);
+    dst[i + half] = f32_to_bf16(bb);
+    return;
   }
-  const int hv0 = max(h0, nq + nkv);   // value heads of this part: [hv0, h1)
-  for (int e = threadIdx.x; e < (h1 - hv0) * hd; e += blockDim.x) {
-    const int h = hv0 + e / hd, d = e % hd;
-    vt[((size_t)(h - nq - nkv) * T + t) * hd + d] = f32_to_bf16(rowv[(h - h0) * hd + d]);
-  }
+  uint16_t* dst = (h < nq) ? q + ((size_t)tok * nq + h) * hd : kt + ((size_t)(h - nq) * T + tok) * hd;
+  dst[i] = f32_to_bf16(a * cs.x - bb * cs.y);
+  dst[i + half] = f32_to_bf16(bb * cs.x + a * cs.y);
 }
 
 namespace {
-int sv_km(int width) {
-  const int need = (width + SV_THREADS - 1) / SV_THREADS;
-  return need <= 2 ? 2 : need <= 4 ? 4 : need <= 6 ? 6 : 8;
-}
 // the kernels' 32-bit ownership arithmetic
 bool sv_fits(const SplitView& v) {
   return v.sk_units * (long long)std::max(v.G_sk, 1) < (1LL << 31) && v.nsteps > 0;
@@ -304,20 +283,19 @@ hipError_t launch_row_stats(const float* h32, int T, int H, const uint16_t* gain
   return hipGetLastError();
 }
 
-hipError_t launch_qkv_rope(const SplitView& v, const float* qkv32, const int32_t* depth, int T, int C,
-                           int nq, int nkv, int hd, float theta, uint16_t* q, uint16_t* kt,
-                           uint16_t* vt, hipStream_t st) {
-  const int NH = nq + 2 * nkv;
-  const int width = ((NH + SV_PARTS - 1) / SV_PARTS) * hd;   // the widest part
-  if (width > SV_MAX_PART || v.rb_count > SV_MAX_BLOCKS || hd > 128 || !sv_fits(v)) return hipErrorInvalidValue;
-  const double th = theta;
-  const dim3 grid(T, SV_PARTS);
-  switch (sv_km(width)) {
-    case 2: hipLaunchKernelGGL(qkv_rope_kernel<2>, grid, dim3(SV_THREADS), 0, st, v, qkv32, depth, T, C, nq, nkv, hd, th, q, kt, vt); break;
-    case 4: hipLaunchKernelGGL(qkv_rope_kernel<4>, grid, dim3(SV_THREADS), 0, st, v, qkv32, depth, T, C, nq, nkv, hd, th, q, kt, vt); break;
-    case 6: hipLaunchKernelGGL(qkv_rope_kernel<6>, grid, dim3(SV_THREADS), 0, st, v, qkv32, depth, T, C, nq, nkv, hd, th, q, kt, vt); break;
-    default: hipLaunchKernelGGL(qkv_rope_kernel<8>, grid, dim3(SV_THREADS), 0, st, v, qkv32, depth, T, C, nq, nkv, hd, th, q, kt, vt); break;
-  }
+hipError_t launch_rope_table(const int32_t* depth, int T, int C, int hd, float theta, float2* rope,
+                             hipStream_t st) {
+  if (hd > 128 || (hd & 1)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rope_table_kernel, dim3(T), dim3(64), 0, st, depth, C, hd, (double)theta, rope);
+  return hipGetLastError();
+}
+
+hipError_t launch_qkv_finish(const SplitView& v, const float* qkv32, const float2* rope, int T, int nq, int nkv,
+                             int hd, uint16_t* q, uint16_t* kt, uint16_t* vt, hipStream_t st) {
+  const int W = (nq + 2 * nkv) * hd;
+  if ((hd != 64 && hd != 128) || !sv_fits(v) || v.rows_per_block % 16) return hipErrorInvalidValue;
+  const dim3 grid(4 * ((W + 127) / 128), (T + 15) / 16);
+  hipLaunchKernelGGL(qkv_finish_kernel, grid, dim3(256), 0, st, v, qkv32, rope, T, nq, nkv, hd, q, kt, vt);
   return hipGetLastError();
 }
 
@@ -371,13 +349,6 @@ hipError_t launch_rmsnorm(const float* h32, const uint16_t* gain, int R, int H, 
                           hipStream_t st) {
   hipLaunchKernelGGL(rmsnorm_kernel, dim3(R), dim3(256), 0, st, h32, gain, H, eps, out, rows,
                      src_rows, err);
-  return hipGetLastError();
-}
-hipError_t launch_rope_split(const float* qkv, const int32_t* depth, int T, int C, int nq, int nkv,
-                             int hd, float theta, uint16_t* q, uint16_t* kt, uint16_t* vt,
-                             hipStream_t st) {
-  hipLaunchKernelGGL(rope_split_kernel, dim3(T), dim3(256), 0, st, qkv, depth, T, C, nq, nkv, hd,
-                     (double)theta, q, kt, vt);
   return hipGetLastError();
 }
 
