@@ -64,11 +64,21 @@ hipError_t launch_tree_mask(const int32_t* parents, int T, uint64_t* mask, int32
 
 // ------------------------------------------------------------------ attention
 
+// One query tile per row wave (short contexts): NKQ1 key groups of NSUB1 sub-tiles each.
+// Several query tiles per row wave (long contexts): one key group of NSUB sub-tiles.
 #ifndef SS_ATTN_NSUB
 #define SS_ATTN_NSUB 2
 #endif
-constexpr int ATT_NSUB = SS_ATTN_NSUB;   // 32-key sub-tiles per K/V tile
-constexpr int ATT_KT = 32 * ATT_NSUB;
+#ifndef SS_ATTN_NSUB1
+#define SS_ATTN_NSUB1 1
+#endif
+#ifndef SS_ATTN_NKQ1
+#define SS_ATTN_NKQ1 4
+#endif
+constexpr int ATT_NSUB = SS_ATTN_NSUB;
+constexpr int ATT_NSUB1 = SS_ATTN_NSUB1;
+constexpr int ATT_NKQ1 = SS_ATTN_NKQ1;
+static int attn_kt(int qc) { return qc == 1 ? 32 * ATT_NSUB1 * ATT_NKQ1 : 32 * ATT_NSUB; }
 
 struct AttnParams {
   const uint16_t* q;
@@ -84,23 +94,33 @@ struct AttnParams {
   float* ml_part;                          // [splits][nkv][rows][2]  (max in log2 units, sum)
 };
 
-template <int HD, int QC, int NSUB>
-__global__ __launch_bounds__(256) void tree_attn_kernel(AttnParams p) {
-  constexpr int NW = 4;
-  constexpr int KT = 32 * NSUB;             // keys per tile: NSUB sub-tiles of 32
+// Workgroup = NR row waves x NKQ key groups. Row wave rw owns QC 16-row query tiles; key
+// group kq takes sub-tiles kq NSUB .. kq NSUB + NSUB - 1 (32 keys each) of every K/V tile,
+// with its own online-softmax state. The key groups of a row wave are combined in LDS at
+// the end, in fixed order, so more waves share the work of a tile without adding partials.
+template <int HD, int QC, int NSUB, int NKQ>
+__global__ __launch_bounds__(256 * NKQ) void tree_attn_kernel(AttnParams p) {
+  constexpr int NR = 4;
+  constexpr int NW = NR * NKQ;
+  constexpr int KT = 32 * NSUB * NKQ;       // keys per tile: NSUB sub-tiles of 32 per key group
   constexpr int VT_STRIDE = KT + 2;         // halfs per transposed-V row: (KT + 2) / 2 words,
                                             // odd, so key-pair writes of a wave spread over banks
   constexpr int HC = HD / 32;               // 32-wide hd chunks
   constexpr int DT = HD / 16;               // 16-wide d tiles of the output
   constexpr int K_STRIDE = HD + 8;          // halfs per K row in LDS (pad against bank conflicts)
-  __shared__ __align__(16) uint16_t k_lds[2][KT * K_STRIDE];
-  __shared__ __align__(16) uint16_t vt_lds[2][HD * VT_STRIDE];
+  constexpr int KV_BYTES = 2 * (KT * K_STRIDE + HD * VT_STRIDE) * 2;
+  constexpr int XC_FLOATS = (NKQ - 1) * NR * QC * (DT * 256 + 128);   // key-group exchange
+  constexpr int SMEM = KV_BYTES > XC_FLOATS * 4 ? KV_BYTES : XC_FLOATS * 4;
+  __shared__ __align__(16) char smem[SMEM];
+  auto k_lds = reinterpret_cast<uint16_t(*)[KT * K_STRIDE]>(smem);
+  auto vt_lds = reinterpret_cast<uint16_t(*)[HD * VT_STRIDE]>(smem + 2 * KT * K_STRIDE * 2);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rw = wave % NR, kq = wave / NR;
   const int j = lane & 15, b = lane >> 4;
   const int kv = blockIdx.y;
   const int split = blockIdx.z;
-  const int row_block = blockIdx.x * NW * QC * 16 + wave * QC * 16;
+  const int row_block = blockIdx.x * NR * QC * 16 + rw * QC * 16;
   const int W = (p.T + 63) >> 6;   // mask words per row
   const int key_begin = split * p.keys_per_split;
   const int key_end = min(p.C + p.T, key_begin + p.keys_per_split);
@@ -230,7 +250,8 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnParams p) {
     for (int kt = 0; kt < 2 * NSUB; ++kt) {
 #pragma unroll
       for (int hc = 0; hc < HC; ++hc) {
-        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(&kl[(kt * 16 + j) * K_STRIDE + hc * 32 + b * 8]);
+        const u32x4_t kf =
+            *reinterpret_cast<const u32x4_t*>(&kl[((kq * 2 * NSUB + kt) * 16 + j) * K_STRIDE + hc * 32 + b * 8]);
         const bf16x8_t ka = __builtin_bit_cast(bf16x8_t, kf);
 #pragma unroll
         for (int c = 0; c < QC; ++c)
@@ -258,7 +279,7 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnParams p) {
         for (int kt = 0; kt < 2 * NSUB; ++kt)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int kk = k0 + kt * 16 + 4 * b + e;
+            const int kk = k0 + (kq * 2 * NSUB + kt) * 16 + 4 * b + e;
             const int jn = kk - p.C;   // tree index (negative in the prefix)
             const uint64_t mw = jn < 64 ? mw0[c] : jn < 128 ? mw1[c] : jn < 192 ? mw2[c] : mw3[c];
             const bool vis = kk < key_end && (jn < 0 || ((mw >> (jn & 63)) & 1ull));
@@ -312,7 +333,8 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnParams p) {
 #pragma unroll
         for (int d = 0; d < DT; ++d) {
           // A operand V^T: lane (i = d row, b) element e' <-> the same key permutation
-          const uint32_t* vrow = reinterpret_cast<const uint32_t*>(&vl[(d * 16 + j) * VT_STRIDE + 32 * sub]);
+          const uint32_t* vrow =
+              reinterpret_cast<const uint32_t*>(&vl[(d * 16 + j) * VT_STRIDE + 32 * (kq * NSUB + sub)]);
           const u32x2_t lo = {vrow[2 * b], vrow[2 * b + 1]};
           const u32x2_t hi = {vrow[8 + 2 * b], vrow[8 + 2 * b + 1]};
           const bf16x8_t va = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
@@ -323,6 +345,58 @@ __global__ __launch_bounds__(256) void tree_attn_kernel(AttnParams p) {
     if (has_next) store_tile(buf ^ 1);   // the other buffer: last read before the previous barrier
     __syncthreads();
     buf ^= 1;
+  }
+
+  // ---- combine the key groups of each row wave, fixed order kq = 0, 1, ...; the loop's
+  // last barrier has passed, so the K / V buffers are free for the exchange
+  if constexpr (NKQ > 1) {
+    float* xo = reinterpret_cast<float*>(smem);          // [NKQ-1][NR][QC][DT][64][4]
+    float* xml = xo + (NKQ - 1) * NR * QC * DT * 256;    // [NKQ-1][NR][QC][64][2]
+    if (kq > 0) {
+#pragma unroll
+      for (int c = 0; c < QC; ++c) {
+        const int slot = ((kq - 1) * NR + rw) * QC + c;
+#pragma unroll
+        for (int d = 0; d < DT; ++d) *reinterpret_cast<f32x4_t*>(&xo[(slot * DT + d) * 256 + lane * 4]) = o[c][d];
+        xml[slot * 128 + lane * 2 + 0] = m_run[c];
+        xml[slot * 128 + lane * 2 + 1] = l_run[c];
+      }
+    }
+    __syncthreads();
+    if (kq > 0) return;
+#pragma unroll
+    for (int c = 0; c < QC; ++c) {
+      float mq[NKQ], lq[NKQ];
+      mq[0] = m_run[c];
+      lq[0] = l_run[c];
+      float M = mq[0];
+#pragma unroll
+      for (int q = 1; q < NKQ; ++q) {
+        const int slot = ((q - 1) * NR + rw) * QC + c;
+        mq[q] = xml[slot * 128 + lane * 2 + 0];
+        lq[q] = xml[slot * 128 + lane * 2 + 1];
+        M = fmaxf(M, mq[q]);
+      }
+      const float Mu = (M == -INFINITY) ? 0.f : M;
+      float f[NKQ], L = 0.f;
+#pragma unroll
+      for (int q = 0; q < NKQ; ++q) {
+        f[q] = exp2f(mq[q] - Mu);   // 0 for a group that saw no visible key
+        L += lq[q] * f[q];
+      }
+#pragma unroll
+      for (int d = 0; d < DT; ++d) {
+        f32x4_t acc = o[c][d] * f[0];
+#pragma unroll
+        for (int q = 1; q < NKQ; ++q) {
+          const int slot = ((q - 1) * NR + rw) * QC + c;
+          acc += *reinterpret_cast<const f32x4_t*>(&xo[(slot * DT + d) * 256 + lane * 4]) * f[q];
+        }
+        o[c][d] = acc;
+      }
+      m_run[c] = M;
+      l_run[c] = L;
+    }
   }
 
   // ---- partials: lane (j, b) holds O^T[d = dt*16 + 4b + e][row j]
@@ -378,17 +452,18 @@ AttnPlan plan_attention(int T, int C, int nq, int nkv, int hd) {
   AttnPlan pl;
   const int grp = nq / nkv;
   const int rows = grp * T;
-  // query-row blocks of 4 waves x QC x 16 rows; QC picked at launch from rows
+  // query-row blocks of 4 row waves x QC x 16 rows; QC picked at launch from rows
   const int qc = attn_qc(rows, C + T);
+  const int KT = attn_kt(qc);
   pl.qblocks = (rows + 4 * qc * 16 - 1) / (4 * qc * 16);
   const int keys = C + T;
   const int units = pl.qblocks * nkv;
-  // aim for ~256 workgroups, keep >= 4 key tiles per split
+  // aim for ~256 workgroups (one per compute unit), at least one key tile per split
   int splits = std::max(1, 256 / std::max(1, units));
-  const int max_splits = std::max(1, keys / (2 * ATT_KT));
+  const int max_splits = std::max(1, keys / KT);
   splits = std::min(splits, max_splits);
   int kps = (keys + splits - 1) / splits;
-  kps = (kps + ATT_KT - 1) / ATT_KT * ATT_KT;
+  kps = (kps + KT - 1) / KT * KT;
   pl.keys_per_split = kps;
   pl.splits = (keys + kps - 1) / kps;
   pl.ws_bytes = (size_t)pl.splits * nkv * rows * (hd + 2) * sizeof(float);
@@ -408,14 +483,16 @@ hipError_t launch_attention(const AttnArgs& a, const AttnPlan& pl, void* ws, hip
   p.ml_part = p.o_part + (size_t)pl.splits * a.nkv * p.rows * a.hd;
   const int qc = attn_qc(p.rows, a.C + a.T);
   dim3 grid(pl.qblocks, a.nkv, pl.splits);
+  if (pl.keys_per_split % attn_kt(qc)) return hipErrorInvalidValue;   // a plan for another shape
+  const dim3 blk1(256 * ATT_NKQ1), blk(256);
   if (a.hd == 128) {
-    if (qc == 1) hipLaunchKernelGGL((tree_attn_kernel<128, 1, ATT_NSUB>), grid, dim3(256), 0, st, p);
-    else if (qc == 2) hipLaunchKernelGGL((tree_attn_kernel<128, 2, ATT_NSUB>), grid, dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((tree_attn_kernel<128, 3, ATT_NSUB>), grid, dim3(256), 0, st, p);
+    if (qc == 1) hipLaunchKernelGGL((tree_attn_kernel<128, 1, ATT_NSUB1, ATT_NKQ1>), grid, blk1, 0, st, p);
+    else if (qc == 2) hipLaunchKernelGGL((tree_attn_kernel<128, 2, ATT_NSUB, 1>), grid, blk, 0, st, p);
+    else hipLaunchKernelGGL((tree_attn_kernel<128, 3, ATT_NSUB, 1>), grid, blk, 0, st, p);
   } else {
-    if (qc == 1) hipLaunchKernelGGL((tree_attn_kernel<64, 1, ATT_NSUB>), grid, dim3(256), 0, st, p);
-    else if (qc == 2) hipLaunchKernelGGL((tree_attn_kernel<64, 2, ATT_NSUB>), grid, dim3(256), 0, st, p);
-    else hipLaunchKernelGGL((tree_attn_kernel<64, 3, ATT_NSUB>), grid, dim3(256), 0, st, p);
+    if (qc == 1) hipLaunchKernelGGL((tree_attn_kernel<64, 1, ATT_NSUB1, ATT_NKQ1>), grid, blk1, 0, st, p);
+    else if (qc == 2) hipLaunchKernelGGL((tree_attn_kernel<64, 2, ATT_NSUB, 1>), grid, blk, 0, st, p);
+    else hipLaunchKernelGGL((tree_attn_kernel<64, 3, ATT_NSUB, 1>), grid, blk, 0, st, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
