@@ -391,10 +391,11 @@ def main():
     inv_t = float(np.float32(1.0) / np.float32(DRAFT_TEMP))
     ws_d = torch.empty(draft.workspace_bytes(T, C), dtype=torch.uint8, device=dev)
     ws_t = torch.empty(target.workspace_bytes(T, C), dtype=torch.uint8, device=dev)
+    ws_s = torch.empty(max(1, bq.draft_select_workspace_bytes(T, V, TOPK)), dtype=torch.uint8, device=dev)
 
     def draft_step():
         draft.draft_tree_step(parents, C, tk_d, tv_d, tokens=tokens, logits=logits, workspace=ws_d)
-        bq.draft_select(logits, None, inv_t, TOPK, out=children)
+        bq.draft_select(logits, None, inv_t, TOPK, out=children, workspace=ws_s)
 
     kc_all = [ly["k_cache"] for ly in target.layers]
     vc_all = [ly["v_cache"] for ly in target.layers]

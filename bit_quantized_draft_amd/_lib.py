@@ -91,8 +91,9 @@ SIGNATURES = {
     "ss_row_argmax": (c_int, [c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
     "ss_tree_accept": (c_int, [c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
                                c_void_p, c_void_p]),
+    "ss_draft_select_workspace": (c_size_t, [c_int32, c_int32, c_int32]),
     "ss_draft_select": (c_int, [c_void_p, c_void_p, c_int32, c_int32, c_float, c_int32, c_void_p,
-                                c_void_p]),
+                                c_void_p, c_size_t, c_void_p]),
 }
 
 _lib = None

@@ -221,13 +221,20 @@ def tree_accept(parents, tokens, target_argmax, out=None):
     return path, ln, bonus
 
 
-def draft_select(logits, gumbel, inv_temp, k, out=None):
+def draft_select(logits, gumbel, inv_temp, k, out=None, workspace=None):
     _need(logits, torch.float32, "logits")
     R, V = logits.shape
     out = torch.empty((R, k), dtype=torch.int32, device=logits.device) if out is None else out
+    nbytes = lib().ss_draft_select_workspace(R, V, k)
+    ws = _workspace(nbytes, logits.device, workspace)
     check(lib().ss_draft_select(_ptr(logits), _ptr(gumbel), R, V, float(inv_temp), k, _ptr(out),
-                                _stream()))
+                                _ptr(ws), nbytes, _stream()))
     return out
+
+
+def draft_select_workspace_bytes(rows, vocab, k):
+    """Workspace bytes ss_draft_select needs for this shape (0: none)."""
+    return lib().ss_draft_select_workspace(rows, vocab, k)
 
 
 # ------------------------------------------------------------------ the draft step
@@ -316,4 +323,4 @@ class SubstituteModel:
 __all__ = ["abi_version", "quantize_substitute", "dequantize_substitute", "w4a16_linear",
            "w4a16_gate_up_swiglu", "TiledW4", "w4_tile", "w4a16_linear_tiled", "w4a16_gate_up_swiglu_tiled",
            "bf16_linear", "tree_validate", "tree_mask", "tree_attention", "row_argmax",
-           "tree_accept", "kv_commit", "draft_select", "SubstituteModel", "SubspecError"]
+           "tree_accept", "kv_commit", "draft_select", "draft_select_workspace_bytes", "SubstituteModel", "SubspecError"]

@@ -746,19 +746,35 @@ ss_status ss_kv_commit(void* const* k_cache, void* const* v_cache, const void* c
   return launched(fn, hipSuccess, st);
 }
 
-ss_status ss_draft_select(const float* logits, const float* gumbel, int32_t rows, int32_t vocab,
-                          float inv_temp, int32_t k, int32_t* tokens_out, void* stream) {
-  const char* fn = __func__;
+static ss_status select_sizes(const char* fn, int32_t rows, int32_t vocab, int32_t k) {
   if (rows < 1 || vocab < 1) return fail(SS_ERR_INVALID_ARG, "%s: rows and vocab must be positive", fn);
   if (rows > 65535) return fail(SS_ERR_UNSUPPORTED, "%s: rows must be <= 65535", fn);
   if (k < 1 || k > 16) return fail(SS_ERR_UNSUPPORTED, "%s: k must be in 1..16 (got %d)", fn, k);
   if (vocab < k) return fail(SS_ERR_INVALID_ARG, "%s: vocab < k", fn);
+  return SS_OK;
+}
+
+size_t ss_draft_select_workspace(int32_t rows, int32_t vocab, int32_t k) {
+  if (select_sizes("ss_draft_select_workspace", rows, vocab, k) != SS_OK) return 0;
+  return ss::draft_select_ws_bytes(rows, vocab, k);
+}
+
+ss_status ss_draft_select(const float* logits, const float* gumbel, int32_t rows, int32_t vocab,
+                          float inv_temp, int32_t k, int32_t* tokens_out, void* workspace,
+                          size_t ws_bytes, void* stream) {
+  const char* fn = __func__;
+  ss_status s0 = select_sizes(fn, rows, vocab, k);
+  if (s0 != SS_OK) return s0;
+  const size_t need = ss::draft_select_ws_bytes(rows, vocab, k);
+  if (need > 0 && (!workspace || ws_bytes < need))
+    return fail(SS_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace ? ws_bytes : 0);
+  if (need > 0) REQ_PTR(workspace, 16);
   if (!(inv_temp > 0.f) || std::isinf(inv_temp)) return fail(SS_ERR_INVALID_ARG, "%s: inv_temp must be finite and > 0", fn);
   REQ_PTR(logits, 4); OPT_PTR(gumbel, 4); REQ_PTR(tokens_out, 4);
   ss_status s = check_device(fn);
   if (s != SS_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return launched(fn, ss::launch_draft_select(logits, gumbel, rows, vocab, inv_temp, k, tokens_out, st), st);
+  return launched(fn, ss::launch_draft_select(logits, gumbel, rows, vocab, inv_temp, k, tokens_out, workspace, st), st);
 }
 
 }  // extern "C"

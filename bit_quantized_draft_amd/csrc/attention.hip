@@ -441,10 +441,22 @@ __global__ __launch_bounds__(HD) void attn_merge_kernel(AttnParams p, uint16_t* 
 }
 
 // 16-row query tiles per wave. Measured on MI355X: one tile per wave (more workgroups,
-// fewer registers) is fastest up to ~4K keys; long contexts favour three (fewer
-// workgroups re-reading each K/V tile).
+// fewer registers) is fastest up to ~4K keys; long contexts favour three while one
+// workgroup then covers all query rows of a KV head (fewer workgroups re-reading each
+// K/V tile), and two once the rows need several workgroups anyway (1280 rows over 4352
+// keys: 142 us against 163 us with three).
+// Tuning overrides (build-time): SS_ATTN_QC forces the query tiles per wave (0 = the rule
+// below); SS_ATTN_WGS is the workgroup count the key split aims for. Measured at the
+// Qwen2.5-7B / Llama-3.1-8B shapes, 128 and 512 workgroups are no faster than 256.
+#ifndef SS_ATTN_QC
+#define SS_ATTN_QC 0
+#endif
+#ifndef SS_ATTN_WGS
+#define SS_ATTN_WGS 256
+#endif
 static int attn_qc(int rows, int keys) {
-  const int qc = (rows <= 64) ? 1 : (rows <= 128) ? 2 : 3;
+  if (SS_ATTN_QC > 0) return SS_ATTN_QC;
+  const int qc = (rows <= 64) ? 1 : (rows <= 128) ? 2 : (rows <= 192) ? 3 : 2;
   return keys <= 4096 ? 1 : qc;
 }
 
@@ -459,7 +471,7 @@ AttnPlan plan_attention(int T, int C, int nq, int nkv, int hd) {
   const int keys = C + T;
   const int units = pl.qblocks * nkv;
   // aim for ~256 workgroups (one per compute unit), at least one key tile per split
-  int splits = std::max(1, 256 / std::max(1, units));
+  int splits = std::max(1, SS_ATTN_WGS / std::max(1, units));
   const int max_splits = std::max(1, keys / KT);
   splits = std::min(splits, max_splits);
   int kps = (keys + splits - 1) / splits;

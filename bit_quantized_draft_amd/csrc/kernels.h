@@ -139,7 +139,9 @@ hipError_t launch_rmsnorm(const float* h32, const uint16_t* gain, int R, int H, 
 // selection / acceptance
 hipError_t launch_row_argmax(const float* logits, int rows, int vocab, int32_t* out, hipStream_t st);
 hipError_t launch_draft_select(const float* logits, const float* gumbel, int rows, int vocab,
-                               float inv_temp, int k, int32_t* out, hipStream_t st);
+                               float inv_temp, int k, int32_t* out, void* ws, hipStream_t st);
+// workspace bytes of launch_draft_select (0: one pass, no workspace)
+size_t draft_select_ws_bytes(int rows, int vocab, int k);
 hipError_t launch_tree_accept(const int32_t* parents, const int32_t* tokens, const int32_t* tgt,
                               int T, int32_t* path, int32_t* len, int32_t* bonus, hipStream_t st);
 

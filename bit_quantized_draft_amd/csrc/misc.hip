@@ -11,6 +11,8 @@
 #include "kernels.h"
 #include "split_view.h"
 
+#include <algorithm>
+
 namespace ss {
 
 // ------------------------------------------------------------------ glue
@@ -448,6 +450,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void row_argmax_kernel(const float* _
 // ------------------------------------------------------------------ draft selection
 
 constexpr int SEL_MAX = 16;
+constexpr int SELECT_MAX_PARTS = 32;   // parts per row of the split selection
 
 // KM: length of each thread's sorted candidate list (>= k); the kernel is instantiated
 // for a few list lengths so the common k = 6 does not pay for 16-entry insertions.
@@ -489,12 +492,138 @@ __global__ __launch_bounds__(SCAN_THREADS) void draft_select_kernel(const float*
   }
 }
 
+// Rows split across workgroups: a row needs ~1.2 MB of logits and noise per draft step
+// at Qwen2.5's vocabulary, and one workgroup per row (64 rows: 64 CUs) is bound by one
+// CU's load rate. Part p of a row scans elements [p seg, (p + 1) seg) and writes its k
+// best (value, index) pairs, best first; a missing entry is (-inf, INT_MAX), which every
+// element beats under the same total order. The k best of a row are among the union of
+// its parts' k best, so the merge reproduces the single-pass result exactly.
+template <int KM>
+__global__ __launch_bounds__(SCAN_THREADS) void draft_select_part_kernel(const float* __restrict__ logits,
+                                                                         const float* __restrict__ gumbel,
+                                                                         int vocab, float inv_temp, int k, int seg,
+                                                                         float* __restrict__ cand_v,
+                                                                         int32_t* __restrict__ cand_i) {
+  const int row = blockIdx.y, part = blockIdx.x, parts = gridDim.x;
+  const int lo = part * seg;
+  const int n = min(vocab, lo + seg) - lo;   // >= 1: the host sizes parts to cover the row
+  const size_t off = (size_t)row * vocab + lo;
+  float tv[KM];
+  int ti[KM];
+#pragma unroll
+  for (int s = 0; s < KM; ++s) { tv[s] = -INFINITY; ti[s] = 0x7FFFFFFF; }
+  scan_row(logits + off, gumbel ? gumbel + off : nullptr, n, inv_temp, [&](float y, int i) {
+    i += lo;
+    if (!better(y, i, tv[KM - 1], ti[KM - 1])) return;
+    float cv = y;
+    int ci = i;
+#pragma unroll
+    for (int s = 0; s < KM; ++s) {
+      if (better(cv, ci, tv[s], ti[s])) {
+        const float xv = tv[s];
+        const int xi = ti[s];
+        tv[s] = cv; ti[s] = ci;
+        cv = xv; ci = xi;
+      }
+    }
+  });
+  const size_t o = ((size_t)row * parts + part) * k;
+  for (int r = 0; r < k; ++r) {
+    const ArgBest w = block_best(tv[0], ti[0]);
+    if (threadIdx.x == 0) { cand_v[o + r] = w.v; cand_i[o + r] = w.i; }
+    if (ti[0] == w.i) {
+#pragma unroll
+      for (int s = 0; s < KM - 1; ++s) { tv[s] = tv[s + 1]; ti[s] = ti[s + 1]; }
+      tv[KM - 1] = -INFINITY;
+      ti[KM - 1] = 0x7FFFFFFF;
+    }
+  }
+}
+
+// One wave per row: k rounds of picking the best remaining candidate of the row's parts.
+// Candidate indices are distinct (the parts cover disjoint ranges) except for the
+// (-inf, INT_MAX) fillers, which only win once every real candidate is taken.
+__global__ __launch_bounds__(64) void draft_select_merge_kernel(const float* __restrict__ cand_v,
+                                                                const int32_t* __restrict__ cand_i, int parts,
+                                                                int k, int32_t* __restrict__ out) {
+  constexpr int CM = SELECT_MAX_PARTS * SEL_MAX / 64;   // candidates per lane
+  const int row = blockIdx.x, lane = threadIdx.x;
+  const int n = parts * k;
+  const size_t o = (size_t)row * n;
+  float cv[CM];
+  int ci[CM];
+#pragma unroll
+  for (int c = 0; c < CM; ++c) {
+    const int e = lane + 64 * c;
+    cv[c] = e < n ? cand_v[o + e] : -INFINITY;
+    ci[c] = e < n ? cand_i[o + e] : 0x7FFFFFFF;
+  }
+  for (int r = 0; r < k; ++r) {
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF, bc = -1;
+#pragma unroll
+    for (int c = 0; c < CM; ++c)
+      if (bc < 0 || better(cv[c], ci[c], bv, bi)) { bv = cv[c]; bi = ci[c]; bc = c; }
+    float wv = bv;
+    int wi = bi;
+#pragma unroll
+    for (int sh = 32; sh > 0; sh >>= 1) {
+      const float ov = __shfl_xor(wv, sh, 64);
+      const int oi = __shfl_xor(wi, sh, 64);
+      if (better(ov, oi, wv, wi)) { wv = ov; wi = oi; }
+    }
+    if (lane == 0) out[(size_t)row * k + r] = wi;
+    // the owner retires the winner; a filler winner (index INT_MAX) leaves only fillers
+    if (bi == wi && bv == wv) {
+#pragma unroll
+      for (int c = 0; c < CM; ++c)
+        if (c == bc) { cv[c] = -INFINITY; ci[c] = 0x7FFFFFFF; }
+    }
+  }
+}
+
+int select_parts(int rows, int vocab, int k) {
+  // about 512 workgroups in all, parts of at least 4096 elements and at least k
+  int parts = std::max(1, std::min(SELECT_MAX_PARTS, (512 + rows - 1) / rows));
+  parts = std::min(parts, std::max(1, vocab / std::max(4096, k)));
+  return parts;
+}
+
+size_t draft_select_ws_bytes(int rows, int vocab, int k) {
+  const int parts = select_parts(rows, vocab, k);
+  if (parts == 1) return 0;
+  const size_t n = (size_t)rows * parts * k;
+  return ((n * sizeof(float) + 255) & ~(size_t)255) + n * sizeof(int32_t);
+}
+
 hipError_t launch_row_argmax(const float* logits, int rows, int vocab, int32_t* out, hipStream_t st) {
   hipLaunchKernelGGL(row_argmax_kernel, dim3(rows), dim3(SCAN_THREADS), 0, st, logits, vocab, out);
   return hipGetLastError();
 }
 hipError_t launch_draft_select(const float* logits, const float* gumbel, int rows, int vocab,
-                               float inv_temp, int k, int32_t* out, hipStream_t st) {
+                               float inv_temp, int k, int32_t* out, void* ws, hipStream_t st) {
+  const int parts = select_parts(rows, vocab, k);
+  if (parts > 1) {
+    // part length: a multiple of 4 elements, so the parts of a 16-byte aligned row keep
+    // the vector loads; ceil(vocab / seg) parts cover the row, none of them empty
+    int seg = (vocab + parts - 1) / parts;
+    seg = (seg + 3) & ~3;
+    const int np = (vocab + seg - 1) / seg;
+    const size_t n = (size_t)rows * np * k;
+    float* cv = static_cast<float*>(ws);
+    int32_t* ci = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + ((n * sizeof(float) + 255) & ~(size_t)255));
+    const dim3 grid(np, rows);
+    if (k <= 2)
+      hipLaunchKernelGGL(draft_select_part_kernel<2>, grid, dim3(SCAN_THREADS), 0, st, logits, gumbel, vocab, inv_temp, k, seg, cv, ci);
+    else if (k <= 6)
+      hipLaunchKernelGGL(draft_select_part_kernel<6>, grid, dim3(SCAN_THREADS), 0, st, logits, gumbel, vocab, inv_temp, k, seg, cv, ci);
+    else
+      hipLaunchKernelGGL(draft_select_part_kernel<SEL_MAX>, grid, dim3(SCAN_THREADS), 0, st, logits, gumbel, vocab, inv_temp, k, seg, cv, ci);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(draft_select_merge_kernel, dim3(rows), dim3(64), 0, st, cv, ci, np, k, out);
+    return hipGetLastError();
+  }
   if (k <= 2)
     hipLaunchKernelGGL(draft_select_kernel<2>, dim3(rows), dim3(SCAN_THREADS), 0, st, logits, gumbel, vocab, inv_temp, k, out);
   else if (k <= 6)

@@ -264,9 +264,15 @@ ss_status ss_kv_commit(void* const* k_cache, void* const* v_cache, const void* c
  * two fp32 operations, no FMA; output the k largest y, larger first, equal y by
  * lower index. gumbel fp32 [rows][vocab] (nullable: g = 0, plain top-k).
  * tokens_out int32 [rows][k]. 1 <= k <= 16, vocab >= k, inv_temp > 0.
+ * Long rows are split across workgroups whose per-part k best are merged by a
+ * second kernel (same result bit for bit); the parts' candidates live in the
+ * caller's workspace of ss_draft_select_workspace(rows, vocab, k) bytes (0: no
+ * workspace needed, it may be null). A smaller workspace returns SS_ERR_WORKSPACE.
  * ------------------------------------------------------------------------------ */
+size_t ss_draft_select_workspace(int32_t rows, int32_t vocab, int32_t k);
 ss_status ss_draft_select(const float* logits, const float* gumbel, int32_t rows, int32_t vocab,
-                          float inv_temp, int32_t k, int32_t* tokens_out, void* stream);
+                          float inv_temp, int32_t k, int32_t* tokens_out, void* workspace,
+                          size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

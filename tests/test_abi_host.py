@@ -116,3 +116,18 @@ def test_kv_commit_argument_checks(L):
     assert b"c_stride" in L.ss_last_error()
     assert L.ss_kv_commit(arr, arr, arr, arr, 1, 1, 96, 100, 0, 16, dummy, dummy, None) == _lib.SS_ERR_UNSUPPORTED
     assert L.ss_kv_commit(None, arr, arr, arr, 1, 1, 128, 100, 0, 16, dummy, dummy, None) == _lib.SS_ERR_INVALID_ARG
+
+
+def test_draft_select_workspace_checks(L):
+    dummy = ctypes.c_void_p(16)
+    # long rows are split across workgroups: the candidates need a workspace
+    need = L.ss_draft_select_workspace(64, 152064, 6)
+    assert need > 0
+    assert L.ss_draft_select_workspace(2, 40, 6) == 0          # one pass per row
+    assert L.ss_draft_select_workspace(2, 40, 17) == 0         # k out of range
+    assert L.ss_draft_select(dummy, None, 64, 152064, 5.0, 6, dummy, None, 0, None) \
+        == _lib.SS_ERR_WORKSPACE
+    assert L.ss_draft_select(dummy, None, 64, 152064, 5.0, 6, dummy, dummy, need - 1, None) \
+        == _lib.SS_ERR_WORKSPACE
+    assert L.ss_draft_select(dummy, None, 64, 152064, 5.0, 0, dummy, dummy, need, None) \
+        == _lib.SS_ERR_UNSUPPORTED

@@ -176,9 +176,13 @@ def test_row_argmax_bitexact(R, V):
     assert np.array_equal(got, oracle.row_argmax(lg))
 
 
+# Rows of 4096+ elements are split across workgroups and merged: (48, 128256) and
+# (64, 152064) take 11 and 8 parts, (3, 50001) 12 parts of an odd-length row (scalar
+# loads) with k = 16, (64, 152064, k = 1) the two-entry lists; the short rows one pass.
 @pytest.mark.parametrize("R,V,t,k,noise", [(48, 128256, 0.2, 6, True), (48, 128256, 0.6, 6, True),
                                            (64, 152064, 1.0, 6, False), (5, 40, 0.5, 16, True),
-                                           (2, 6, 0.2, 6, True)])
+                                           (2, 6, 0.2, 6, True), (3, 50001, 0.3, 16, True),
+                                           (64, 152064, 0.2, 1, True)])
 def test_draft_select_bitexact(R, V, t, k, noise):
     rng = np.random.default_rng(V + k)
     lg = (rng.standard_normal((R, V)) * 2).astype(np.float32)
@@ -187,6 +191,25 @@ def test_draft_select_bitexact(R, V, t, k, noise):
     inv_t = np.float32(1.0) / np.float32(t)
     got = host(bq.draft_select(to_dev(lg), None if g is None else to_dev(g), inv_t, k))
     assert np.array_equal(got, oracle.draft_select(lg, g, inv_t, k))
+
+
+@pytest.mark.parametrize("where", ["first", "last", "spread"])
+def test_draft_select_split_extremes(where):
+    """All k winners inside one part (first or last), or one per part: the merge must take
+    every candidate a part offers, and the order of equal values across parts is by index."""
+    R, V, k = 4, 152064, 6
+    rng = np.random.default_rng(7)
+    lg = (rng.standard_normal((R, V))).astype(np.float32)
+    if where == "first":
+        lg[:, 3:3 + k] = 50.0                     # k equal winners in part 0: by index
+    elif where == "last":
+        lg[:, V - k:] = np.arange(k, dtype=np.float32)[::-1] + 40.0
+    else:
+        idx = np.linspace(0, V - 1, k).astype(int)
+        lg[:, idx] = 45.0                         # equal values in different parts
+    got = host(bq.draft_select(to_dev(lg), None, np.float32(1.0), k))
+    want = oracle.draft_select(lg, None, np.float32(1.0), k)
+    assert np.array_equal(got, want)
 
 
 @pytest.mark.parametrize("kind,T,L_star", [("CB", 64, 27), ("CB", 48, 0), ("RB", 256, 5),
