@@ -216,8 +216,8 @@ ss_status check_model(const char* fn, const ss_model* m) {
   for (int l = 0; l < m->L; ++l) {
     const ss_layer& ly = m->layers[l];
     if (!ly.norm1 || !ly.norm2) return fail(SS_ERR_INVALID_ARG, "%s: layer %d: null norm gain", fn, l);
-    if (!ly.k_cache || !ly.v_cache) return fail(SS_ERR_INVALID_ARG, "%s: layer %d: null KV cache", fn, l);
-    if (!aligned(ly.k_cache, 16) || !aligned(ly.v_cache, 16))
+    // a null cache is allowed with an empty prefix (C == 0, checked by the step)
+    if ((ly.k_cache && !aligned(ly.k_cache, 16)) || (ly.v_cache && !aligned(ly.v_cache, 16)))
       return fail(SS_ERR_INVALID_ARG, "%s: layer %d: KV cache not 16-byte aligned", fn, l);
     ss_status s;
     if ((s = check_linear(fn, ly.qkv, "qkv")) != SS_OK) return s;
@@ -536,6 +536,8 @@ ss_status ss_draft_tree_step(const ss_model* m, const ss_step_args* a, void* wor
   REQ_PTR(a->parents, 4);
   if (!a->tree_k || !a->tree_v) return fail(SS_ERR_INVALID_ARG, "%s: tree_k / tree_v arrays are null", fn);
   for (int l = 0; l < m->L; ++l) {
+    if (C > 0 && (!m->layers[l].k_cache || !m->layers[l].v_cache))
+      return fail(SS_ERR_INVALID_ARG, "%s: layer %d: null KV cache with a prefix of %d keys", fn, l, C);
     if (!a->tree_k[l] || !a->tree_v[l]) return fail(SS_ERR_INVALID_ARG, "%s: tree K/V of layer %d is null", fn, l);
     if (!aligned(a->tree_k[l], 16) || !aligned(a->tree_v[l], 16))
       return fail(SS_ERR_INVALID_ARG, "%s: tree K/V of layer %d not 16-byte aligned", fn, l);

@@ -582,9 +582,12 @@ __global__ __launch_bounds__(64) void draft_select_merge_kernel(const float* __r
   }
 }
 
+#ifndef SS_SELECT_WGS
+#define SS_SELECT_WGS 512
+#endif
 int select_parts(int rows, int vocab, int k) {
-  // about 512 workgroups in all, parts of at least 4096 elements and at least k
-  int parts = std::max(1, std::min(SELECT_MAX_PARTS, (512 + rows - 1) / rows));
+  // about SS_SELECT_WGS workgroups in all, parts of at least 4096 elements and at least k
+  int parts = std::max(1, std::min(SELECT_MAX_PARTS, (SS_SELECT_WGS + rows - 1) / rows));
   parts = std::min(parts, std::max(1, vocab / std::max(4096, k)));
   return parts;
 }

@@ -192,7 +192,8 @@ typedef struct {
   ss_linear o;           /* n = H, k = nq hd */
   ss_linear gate_up;     /* n = 2 I, k = H; rows [0, I) gate, [I, 2I) up */
   ss_linear down;        /* n = H, k = I */
-  const void* k_cache;   /* bf16 [nkv][c_stride][hd] (shared with the target, read only) */
+  const void* k_cache;   /* bf16 [nkv][c_stride][hd] (shared with the target, read only;
+                            may be null when the step's prefix is empty, C == 0) */
   const void* v_cache;
 } ss_layer;
 

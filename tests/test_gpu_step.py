@@ -70,6 +70,8 @@ def small_cfg(**kw):
     (dict(nq=4, nkv=4, hd=64, H=256, I=512), 17, 100, "R", "tiled"),
     (dict(H=3584, I=18944, nq=28, nkv=4, hd=128, cid=2), 48, 1024, "CB", "int4"),   # Qwen2.5-7B-shaped layer
     (dict(H=3584, I=18944, nq=28, nkv=4, hd=128, cid=2), 64, 2048, "CB", "tiled"),
+    (dict(nq=4, nkv=4, hd=64, H=256, I=512), 1, 0, "R", "tiled"),       # root only, no prefix
+    (dict(nq=4, nkv=2, hd=64, H=256, I=512), 256, 64, "RB", "tiled"),   # largest tree: 4 token blocks
 ])
 def test_one_layer_parity(cfgkw, T, C, kind, wl):
     cfg = small_cfg(**cfgkw)
