@@ -19,8 +19,11 @@ does; every float reference (matmul, attention, layer) runs in fp64.
 
 Parity pins: every function is pinned by the CPU tests in tests/test_oracle_*.py
 against brute force, closed forms, special cases and library routines. The
-whole-stack composition (`stack64`) has no independent pin beyond its parts and
-is "parity unpinned" as a whole.
+whole-stack composition (`stack64`) is pinned by zero-projection layers (the stack
+reduces to embedding, final norm and head) and by an independent float64
+implementation with torch primitives (complex-rotation RoPE, parent-walk tree mask,
+masked scaled-dot-product attention) over three non-trivial layers with distinct
+caches.
 """
 
 from .fp import bf16_to_f32, bf16_to_f64, f32_to_bf16  # noqa: F401

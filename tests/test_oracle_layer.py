@@ -7,7 +7,11 @@
 - layer: zero o/down weights leave the hidden state unchanged; a single root token
   with no prefix attends only to itself, so the layer reduces to plain matrix
   products, checked in closed form with all four projections;
-- relabelling the tree nodes in another topological order permutes the layer output.
+- relabelling the tree nodes in another topological order permutes the layer output;
+- stack: zero o/down weights reduce it to embedding, final norm and head; three
+  non-trivial layers agree with an independent float64 torch implementation (torch
+  RMSNorm, RoPE as a complex rotation, ancestor mask by walking parents, masked
+  scaled-dot-product attention, SiLU).
 """
 
 import types
@@ -151,3 +155,89 @@ def test_stack_with_zero_output_projections_is_embedding_then_head():
     for r, row in enumerate([1, 4]):
         x = e[row] / np.sqrt(np.mean(e[row] ** 2) + cfg.eps) * g
         np.testing.assert_allclose(logits[r], oracle.bf16_to_f64(head) @ x, rtol=1e-12, atol=1e-12)
+
+
+def _torch_stack_reference(tok, par, C, embed, layers, kcs, vcs, fnorm, head, cfg, rows):
+    """An independent float64 implementation of the substitute stack with torch primitives:
+    torch's RMSNorm, RoPE as a complex rotation of (x_i, x_{i+hd/2}) pairs, the tree mask
+    by walking parent pointers, torch's masked scaled-dot-product attention with the KV
+    heads repeated per query group, and torch's SiLU."""
+    import torch
+    import torch.nn.functional as F
+    f64 = torch.float64
+    bf = lambda bits: torch.from_numpy(oracle.bf16_to_f64(bits))  # bf16 bits -> float64 tensor
+
+    def deq(entry):
+        q, s, z = entry
+        q = torch.from_numpy(q.astype(np.float64))
+        s = torch.from_numpy(s.astype(np.float64)).repeat_interleave(64, dim=1)
+        z = torch.from_numpy(z.astype(np.float64)).repeat_interleave(64, dim=1)
+        return (q - z) * s
+
+    T = len(tok)
+    depth = []
+    for i in range(T):                      # depth by walking parents
+        d, cur = 0, i
+        while par[cur] >= 0:
+            cur, d = int(par[cur]), d + 1
+        depth.append(d)
+    vis = torch.zeros((T, C + T), dtype=torch.bool)
+    vis[:, :C] = True
+    for i in range(T):                      # ancestors-or-self by walking parents
+        cur = i
+        while cur >= 0:
+            vis[i, C + cur] = True
+            cur = int(par[cur])
+    pos = torch.tensor([C + d for d in depth], dtype=f64)
+    half = cfg.hd // 2
+    freq = cfg.rope_theta ** (-torch.arange(half, dtype=f64) * 2.0 / cfg.hd)
+    rot = torch.polar(torch.ones(T, half, dtype=f64), pos[:, None] * freq[None, :])   # e^{i pos f}
+
+    def rope(x):                            # x [T][heads][hd]
+        c = torch.complex(x[..., :half], x[..., half:]) * rot[:, None, :]
+        return torch.cat([c.real, c.imag], dim=-1)
+
+    h = bf(embed)[torch.from_numpy(np.asarray(tok))]
+    grp = cfg.nq // cfg.nkv
+    for li, lw in enumerate(layers):
+        x = F.rms_norm(h, (cfg.H,), weight=bf(lw["norm1"]), eps=cfg.eps)
+        qkv = x @ deq(lw["qkv"]).T
+        q = rope(qkv[:, :cfg.nq * cfg.hd].reshape(T, cfg.nq, cfg.hd))
+        k = rope(qkv[:, cfg.nq * cfg.hd:(cfg.nq + cfg.nkv) * cfg.hd].reshape(T, cfg.nkv, cfg.hd))
+        v = qkv[:, (cfg.nq + cfg.nkv) * cfg.hd:].reshape(T, cfg.nkv, cfg.hd)
+        K = torch.cat([torch.from_numpy(np.asarray(kcs[li], np.float64)[:, :C]), k.transpose(0, 1)], dim=1)
+        Vv = torch.cat([torch.from_numpy(np.asarray(vcs[li], np.float64)[:, :C]), v.transpose(0, 1)], dim=1)
+        K = K.repeat_interleave(grp, dim=0)                                   # [nq][C+T][hd]
+        Vv = Vv.repeat_interleave(grp, dim=0)
+        a = F.scaled_dot_product_attention(q.transpose(0, 1), K, Vv, attn_mask=vis[None])
+        h = h + a.transpose(0, 1).reshape(T, cfg.nq * cfg.hd) @ deq(lw["o"]).T
+        x = F.rms_norm(h, (cfg.H,), weight=bf(lw["norm2"]), eps=cfg.eps)
+        gu = x @ deq(lw["gate_up"]).T
+        h = h + (F.silu(gu[:, :cfg.I]) * gu[:, cfg.I:]) @ deq(lw["down"]).T
+    x = F.rms_norm(h[list(rows)], (cfg.H,), weight=bf(fnorm), eps=cfg.eps)
+    return h.numpy(), (x @ bf(head).T).numpy()
+
+
+def test_stack_matches_an_independent_torch_implementation():
+    """Pins the whole-stack composition: layer order, each layer's own KV cache, positions
+    C + depth, residual adds, final RMSNorm of the selected rows and the LM head."""
+    cfg = _cfg(H=64, I=128, nq=4, nkv=2, hd=16)
+    V, T, C = 40, 11, 7
+    rng = np.random.default_rng(21)
+    embed = gen.bf16_bits(rng.standard_normal((V, cfg.H)))
+    head = gen.bf16_bits(rng.standard_normal((V, cfg.H)) * 0.05)
+    fnorm = gen.norm_gain_bf16(cfg.H, seed=21, random=True)
+    layers = [_layer_weights(cfg, 30 + i) for i in range(3)]
+    kcs = [rng.standard_normal((cfg.nkv, C + 2, cfg.hd)) for _ in range(3)]   # c_stride > C
+    vcs = [rng.standard_normal((cfg.nkv, C + 2, cfg.hd)) for _ in range(3)]
+    tok = rng.integers(0, V, T)
+    par = gen.tree_parents(T, "R", seed=21)
+    rows = [10, 0, 4]
+    h, logits = oracle.stack64(tok, par, C, embed, layers, kcs, vcs, fnorm, head, cfg, logit_rows=rows)
+    h_ref, lg_ref = _torch_stack_reference(tok, par, C, embed, layers, kcs, vcs, fnorm, head, cfg, rows)
+    np.testing.assert_allclose(h, h_ref, rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(logits, lg_ref, rtol=1e-10, atol=1e-10)
+    # swapping two layers changes the result: the composition order is observed
+    h_sw, _ = oracle.stack64(tok, par, C, embed, [layers[1], layers[0], layers[2]],
+                             [kcs[1], kcs[0], kcs[2]], [vcs[1], vcs[0], vcs[2]], fnorm, head, cfg)
+    assert np.abs(h_sw - h).max() > 1e-3
