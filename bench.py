@@ -166,10 +166,11 @@ PMC_MD = os.path.join(ROOT, "profiles", "gate_up_swiglu_qwen7b_T64_pmc.md")
 CAL_BYTES = 256 << 20          # calibration: fp32 negation reads and writes this many bytes
 
 
-def gate_up_bytes(cfg):
+def gate_up_bytes(cfg, T=None):
     """Algorithmic bytes of one gate_up launch: int4 codes + fp16 scale/zero (0.5625 B per
     weight), bf16 activations in, bf16 SwiGLU output."""
-    return 0.5625 * 2 * cfg.I * cfg.H + cfg.T * cfg.H * 2 + cfg.T * cfg.I * 2
+    T = cfg.T if T is None else T
+    return 0.5625 * 2 * cfg.I * cfg.H + T * cfg.H * 2 + T * cfg.I * 2
 
 
 def pmc_probe(args):
@@ -469,15 +470,37 @@ def main():
     step_gbs = step_bytes / (ms_draft_step * 1e-3) / 1e9
 
     # dominant kernel: fused int4 gate_up + SwiGLU, 8 layers' weights in rotation (> 256 MB
-    # Infinity Cache), timed with HIP events recorded on the stream it runs on
+    # Infinity Cache), timed with HIP events recorded on the stream it runs on. The sweep
+    # over tree sizes runs first and also brings the GPU to a steady state; the T = 64
+    # figure of the roofline object is measured last.
     x = gen.torch_normal_bf16((T, cfg.H), 1.0, 0, cfg.cid, gen.TID_X, 0, dev)
     u = torch.empty((T, cfg.I), dtype=torch.bfloat16, device=dev)
     rot = [draft.layers[i % n_layers]["gate_up"] for i in range(8)]
     ks = torch.cuda.Stream()
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # the same kernel over the tree sizes the HBM-bound target covers (16 to 64 tokens),
+    # same weights, same timing method
+    by_tokens = {}
+    for tn in (16, 32, 48, 64):
+        xt = gen.torch_normal_bf16((tn, cfg.H), 1.0, 0, cfg.cid, gen.TID_X, 0, dev)
+        ut = torch.empty((tn, cfg.I), dtype=torch.bfloat16, device=dev)
+        with torch.cuda.stream(ks):
+            for tw in rot:
+                bq.w4a16_gate_up_swiglu_tiled(xt, tw, out=ut)
+            k0.record(ks)
+            for _ in range(args.kernel_reps):
+                for tw in rot:
+                    bq.w4a16_gate_up_swiglu_tiled(xt, tw, out=ut)
+            k1.record(ks)
+        torch.cuda.synchronize()
+        us_t = k0.elapsed_time(k1) * 1e3 / (args.kernel_reps * len(rot))
+        gbs_t = gate_up_bytes(cfg, tn) / (us_t * 1e-6) / 1e9
+        by_tokens[str(tn)] = {"avg_launch_us": round(us_t, 3), "achieved": round(gbs_t, 1),
+                              "frac": round(gbs_t / HBM_PEAK_GBS, 4)}
+
     with torch.cuda.stream(ks):
         for tw in rot:
             bq.w4a16_gate_up_swiglu_tiled(x, tw, out=u)
-        k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         k0.record(ks)
         n_launch = 0
         for _ in range(args.kernel_reps):
@@ -511,7 +534,8 @@ def main():
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profile(gu_bytes),
-                     "alg_bytes_per_launch": int(gu_bytes), "avg_launch_us": round(us_launch, 3)},
+                     "alg_bytes_per_launch": int(gu_bytes), "avg_launch_us": round(us_launch, 3),
+                     "by_tree_tokens": by_tokens},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
