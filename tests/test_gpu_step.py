@@ -4,7 +4,8 @@ One layer is compared with the oracle's fp64 layer from the same bf16 hidden inp
 (tolerance: rel-L2 <= 1e-2, max-abs <= 2e-2 * max(1, rms(ref)) plus, for outputs stored
 in bf16, the storage rounding of half a bf16 ulp of each reference value); the tree K/V
 it writes are compared too. Small stacks with an LM head are compared end to end, including the
-logits of selected rows.
+logits of selected rows. Weights run as plain int4, tiled int4 (the draft) and dense bf16 (the
+target's verify pass).
 """
 
 import types
@@ -72,6 +73,7 @@ def small_cfg(**kw):
     (dict(H=3584, I=18944, nq=28, nkv=4, hd=128, cid=2), 64, 2048, "CB", "tiled"),
     (dict(nq=4, nkv=4, hd=64, H=256, I=512), 1, 0, "R", "tiled"),       # root only, no prefix
     (dict(nq=4, nkv=2, hd=64, H=256, I=512), 256, 64, "RB", "tiled"),   # largest tree: 4 token blocks
+    (dict(H=3584, I=18944, nq=28, nkv=4, hd=128, cid=2), 64, 2048, "CB", "bf16"),   # target verify layer
 ])
 def test_one_layer_parity(cfgkw, T, C, kind, wl):
     cfg = small_cfg(**cfgkw)
@@ -95,7 +97,8 @@ def test_one_layer_parity(cfgkw, T, C, kind, wl):
 
 @pytest.mark.parametrize("L,T,C,V,kind,rows,wl", [(2, 16, 64, 4096, "R", None, "int4"),
                                                   (3, 64, 128, 2048, "CB", [0, 5, 63, 5], "int4"),
-                                                  (3, 64, 128, 2048, "CB", [0, 5, 63, 5], "tiled")])
+                                                  (3, 64, 128, 2048, "CB", [0, 5, 63, 5], "tiled"),
+                                                  (3, 64, 128, 2048, "CB", None, "bf16")])
 def test_small_stack_with_lm_head(L, T, C, V, kind, rows, wl):
     cfg = small_cfg(cid=8, H=256, I=512, nq=4, nkv=2, hd=64)
     layers = [make_layer(cfg, li, C, seed=2, kind=wl) for li in range(L)]
