@@ -131,3 +131,27 @@ def test_draft_select_workspace_checks(L):
         == _lib.SS_ERR_WORKSPACE
     assert L.ss_draft_select(dummy, None, 64, 152064, 5.0, 0, dummy, dummy, need, None) \
         == _lib.SS_ERR_UNSUPPORTED
+
+
+def _dummy_step(C):
+    """A one-layer model and step arguments whose pointers are never dereferenced (the
+    checks fail or stop at the workspace before any device call); no KV cache."""
+    p = 4096   # aligned dummy address
+    lin = _lib.SsLinear(kind=_lib.SS_W4G64_TILED, qweight=p)
+    layers = (_lib.SsLayer * 1)()
+    layers[0] = _lib.SsLayer(norm1=p, norm2=p, qkv=lin, o=lin, gate_up=lin, down=lin,
+                             k_cache=None, v_cache=None)
+    model = _lib.SsModel(H=256, I=512, nq=4, nkv=2, hd=64, L=1, V=0, rope_theta=1e6, rms_eps=1e-6,
+                         c_stride=16, layers=layers)
+    tk = (ctypes.c_void_p * 1)(p)
+    args = _lib.SsStepArgs(parents=p, T=4, C=C, tree_k=tk, tree_v=tk, hidden_in=p, hidden_out=p)
+    return model, args, layers, tk
+
+
+def test_step_kv_cache_may_be_null_only_without_prefix(L):
+    model, args, _keep1, _keep2 = _dummy_step(C=0)
+    # passes every argument check and stops at the missing workspace
+    assert L.ss_draft_tree_step(ctypes.byref(model), ctypes.byref(args), None, 0, None) == _lib.SS_ERR_WORKSPACE
+    model, args, _keep1, _keep2 = _dummy_step(C=5)
+    assert L.ss_draft_tree_step(ctypes.byref(model), ctypes.byref(args), None, 0, None) == _lib.SS_ERR_INVALID_ARG
+    assert b"null KV cache" in L.ss_last_error()
