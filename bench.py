@@ -155,7 +155,7 @@ def cpu_baseline(cfg, n_layers):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("gemm.hip", "common.h", "kernels.h"):
+    for f in ("gemm_w4.hip", "gemm_w4_kernel.h", "common.h", "kernels.h"):
         with open(os.path.join(ROOT, "bit_quantized_draft_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -287,8 +287,8 @@ def pmc_summary(fetch_dir, write_dir):
     out = {}
     for counter, folder in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _counter_rows(folder, counter)
-        gemm = [v for (_, k), v in rows.items() if "w4t_gemm_kernel" in k]
-        red = [v for (_, k), v in rows.items() if "sk_reduce_kernel" in k]
+        gemm = [v for (_, k), v in rows.items() if "w4k_kernel" in k]
+        red = [v for (_, k), v in rows.items() if "w4_reduce_kernel" in k]
         cal = [v for (_, k), v in rows.items() if "neg" in k.lower()]
         if not gemm or len(cal) != 1:
             raise SystemExit(f"{counter}: expected gate_up dispatches and one calibration dispatch, "
@@ -302,7 +302,7 @@ def pmc_summary(fetch_dir, write_dir):
                         "bytes_gemm": g, "bytes_reduce": r, "dispatches": len(gemm)}
     alg = gate_up_bytes(cfg)
     hbm = sum(v["bytes_gemm"] + v["bytes_reduce"] for v in out.values())
-    d = {"kernel": "w4t_gemm_kernel<T=64, EPI_SWIGLU> + sk_reduce_kernel (tiled int4 gate_up 37888x3584, T=64)",
+    d = {"kernel": "w4k_kernel<TT=4, EPI_SWIGLU, tiled> (tiled int4 gate_up 37888x3584, T=64)",
          "source_hash": kernel_source_hash(), "alg_bytes_per_launch": int(alg),
          "hbm_bytes_per_launch": int(hbm), "hbm_over_alg": round(hbm / alg, 4), "counters": out}
     with open(PMC_JSON, "w") as fh:
@@ -318,7 +318,7 @@ def pmc_summary(fetch_dir, write_dir):
         "python3 bench.py --pmc-summary <out>/fetch <out>/write",
         "```",
         "",
-        f"Kernel sources hash (gemm.hip, common.h, kernels.h): `{d['source_hash']}`",
+        f"Kernel sources hash (gemm_w4.hip, gemm_w4_kernel.h, common.h, kernels.h): `{d['source_hash']}`",
         "",
         "| counter | KiB/dispatch GEMM | KiB/dispatch reduce | KiB calibration (256 MiB) | factor | bytes/launch |",
         "|---|---|---|---|---|---|",
@@ -530,7 +530,7 @@ def main():
                    "draft_step_ms": round(ms_draft_step, 4), "verify_ms": round(ms_verify, 4),
                    "draft_step_alg_bytes": int(step_bytes),
                    "draft_step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4)},
-        "roofline": {"kernel": "w4t_gemm_kernel<T=64, EPI_SWIGLU> + sk_reduce_kernel (tiled int4 gate_up 37888x3584, T=64)",
+        "roofline": {"kernel": "w4k_kernel<TT=4, EPI_SWIGLU, tiled> (tiled int4 gate_up 37888x3584, T=64)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_from_profile(gu_bytes),

@@ -13,7 +13,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsubspec.so")
 
-SOURCES = ["gemm.hip", "quant.hip", "attention.hip", "misc.hip", "api.cpp"]
+SOURCES = ["gemm_w4.hip", "gemm_w4_tt1.hip", "gemm_w4_tt2.hip", "gemm_w4_tt3.hip", "gemm_w4_tt4.hip", "gemm_bf16.hip", "quant.hip", "attention.hip", "misc.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -114,21 +114,37 @@ struct Bump {
   }
 };
 
-ss::GemmArgs gemm_args(const void* x, int T, const ss_linear& w, int N, int K) {
-  ss::GemmArgs a{};
+bool is_int4(const ss_linear& w) { return w.kind == SS_W4G64 || w.kind == SS_W4G64_TILED; }
+
+ss::W4Args w4_args(const void* x, int T, const ss_linear& w, int N, int K) {
+  ss::W4Args a{};
   a.x = static_cast<const uint16_t*>(x);
   a.T = T; a.N = N; a.K = K;
-  if (w.kind == SS_W4G64) {
-    a.qw = static_cast<const uint8_t*>(w.qweight);
+  a.qw = static_cast<const uint8_t*>(w.qweight);
+  a.tiled = w.kind == SS_W4G64_TILED;
+  if (!a.tiled) {
     a.sc = static_cast<const uint16_t*>(w.scale);
     a.zp = static_cast<const uint16_t*>(w.zero);
-  } else if (w.kind == SS_W4G64_TILED) {
-    a.qw = static_cast<const uint8_t*>(w.qweight);
-    a.tiled = true;
-  } else {
-    a.wb = static_cast<const uint16_t*>(w.w);
   }
   return a;
+}
+
+ss::GemmArgs bf16_args(const void* x, int T, const void* w, int N, int K) {
+  ss::GemmArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.wb = static_cast<const uint16_t*>(w);
+  a.T = T; a.N = N; a.K = K;
+  return a;
+}
+
+// the bf16 GEMM's bounded hand-off waits: report an expiry (checked under SS_DEBUG_SYNC)
+ss_status check_bf16_waits(const char* fn) {
+  if (!debug_sync()) return SS_OK;
+  int expired = 0;
+  hipError_t e = ss::gemm_bf16_wait_expired(&expired);
+  if (e != hipSuccess) return fail(SS_ERR_DEVICE, "%s: %s", fn, hipGetErrorString(e));
+  if (expired) return fail(SS_ERR_DEVICE, "%s: a bf16 GEMM hand-off wait expired (results invalid)", fn);
+  return SS_OK;
 }
 
 ss_status check_linear(const char* fn, const ss_linear& w, const char* name) {
@@ -186,12 +202,17 @@ StepLayout plan_step(const ss_model* m, int T, int C, int R, void* base) {
   L.attn = bp.take<uint16_t>((size_t)T * m->nq * m->hd);
   L.ubuf = bp.take<uint16_t>((size_t)T * m->I);
   size_t g = 0;
-  auto need = [&](const ss::GemmPlan& pl) { g = std::max(g, pl.ws_bytes); };
-  need(ss::plan_gemm(T, qkvN, m->H, ss::EPI_STORE, 0));
-  need(ss::plan_gemm(T, m->H, m->nq * m->hd, ss::EPI_RESID, 0));
-  need(ss::plan_gemm(T, 2 * m->I, m->H, ss::EPI_SWIGLU, m->I));
-  need(ss::plan_gemm(T, m->H, m->I, ss::EPI_RESID, 0));
-  if (R > 0 && m->V > 0) need(ss::plan_gemm(R, m->V, m->H, ss::EPI_STORE, 0));
+  auto need = [&](size_t bytes) { g = std::max(g, bytes); };
+  // both engines' plans (a model may mix int4 and bf16 linears)
+  need(ss::plan_w4(T, qkvN, m->H, ss::EPI_STORE, 0, false).ws_bytes);
+  need(ss::plan_w4(T, m->H, m->nq * m->hd, ss::EPI_RESID, 0, false).ws_bytes);
+  need(ss::plan_w4(T, 2 * m->I, m->H, ss::EPI_SWIGLU, m->I, true).ws_bytes);
+  need(ss::plan_w4(T, m->H, m->I, ss::EPI_RESID, 0, false).ws_bytes);
+  need(ss::plan_gemm(T, qkvN, m->H, ss::EPI_STORE, 0).ws_bytes);
+  need(ss::plan_gemm(T, m->H, m->nq * m->hd, ss::EPI_RESID, 0).ws_bytes);
+  need(ss::plan_gemm(T, 2 * m->I, m->H, ss::EPI_SWIGLU, m->I).ws_bytes);
+  need(ss::plan_gemm(T, m->H, m->I, ss::EPI_RESID, 0).ws_bytes);
+  if (R > 0 && m->V > 0) need(ss::plan_gemm(R, m->V, m->H, ss::EPI_STORE, 0).ws_bytes);
   L.gemm_ws = bp.take<char>(g);
   L.attn_ws = bp.take<char>(ss::plan_attention(T, C, m->nq, m->nkv, m->hd).ws_bytes);
   L.total = bp.off;
@@ -271,75 +292,97 @@ ss_status ss_dequantize_substitute(const void* qweight, const void* scale, const
 
 // ------------------------------------------------------------------ linear layers
 
+// Shape and pointer checks shared by the linear layers; need = the workspace the plan asks for.
 static ss_status linear_common(const char* fn, const void* x, int32_t T, int64_t n, int64_t k,
-                               void* y_bf16, float* y_f32, void* ws, size_t ws_bytes) {
-  if (T < 1 || T > 256) return fail(SS_ERR_UNSUPPORTED, "%s: T must be in 1..256 (got %d)", fn, T);
-  if (n <= 0 || k <= 0) return fail(SS_ERR_INVALID_ARG, "%s: n and k must be positive", fn);
-  if (k % 128) return fail(SS_ERR_UNSUPPORTED, "%s: k must be a multiple of 128", fn);
-  if (n % 16) return fail(SS_ERR_UNSUPPORTED, "%s: n must be a multiple of 16", fn);
-  if (n > 0x7FFFFFFF / 256 || k > 0x7FFFFFFF / 2) return fail(SS_ERR_UNSUPPORTED, "%s: n or k too large", fn);
+                               void* y_bf16, float* y_f32, void* ws, size_t ws_bytes, size_t need) {
   REQ_PTR(x, 16);
   if (!y_bf16 && !y_f32) return fail(SS_ERR_INVALID_ARG, "%s: y_bf16 and y_f32 are both null", fn);
   OPT_PTR(y_bf16, 2); OPT_PTR(y_f32, 4);
-  const size_t need = ss::plan_gemm(T, (int)n, (int)k, ss::EPI_STORE, 0).ws_bytes;
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(SS_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws ? ws_bytes : 0);
   OPT_PTR(ws, 16);
   return SS_OK;
 }
 
+static ss_status linear_sizes(const char* fn, int32_t T, int64_t n, int64_t k) {
+  if (T < 1 || T > 256) return fail(SS_ERR_UNSUPPORTED, "%s: T must be in 1..256 (got %d)", fn, T);
+  if (n <= 0 || k <= 0) return fail(SS_ERR_INVALID_ARG, "%s: n and k must be positive", fn);
+  if (k % 128) return fail(SS_ERR_UNSUPPORTED, "%s: k must be a multiple of 128", fn);
+  if (n % 16) return fail(SS_ERR_UNSUPPORTED, "%s: n must be a multiple of 16", fn);
+  if (n > 0x7FFFFFFF / 256 || k > 0x7FFFFFFF / 2) return fail(SS_ERR_UNSUPPORTED, "%s: n or k too large", fn);
+  return SS_OK;
+}
+
+static bool linear_shape_ok(int32_t T, int64_t n, int64_t k) {
+  return T >= 1 && T <= 256 && n > 0 && k > 0 && k % 128 == 0 && n % 16 == 0 && n <= 0x7FFFFFFF / 256 &&
+         k <= 0x7FFFFFFF / 2;
+}
+
 size_t ss_w4a16_linear_workspace(int32_t T, int64_t n, int64_t k) {
-  if (T < 1 || n <= 0 || k < 128) return 0;
+  if (!linear_shape_ok(T, n, k)) return 0;
+  return ss::plan_w4(T, (int)n, (int)k, ss::EPI_STORE, 0, true).ws_bytes;
+}
+size_t ss_bf16_linear_workspace(int32_t T, int64_t n, int64_t k) {
+  if (!linear_shape_ok(T, n, k)) return 0;
   return ss::plan_gemm(T, (int)n, (int)k, ss::EPI_STORE, 0).ws_bytes;
 }
-size_t ss_bf16_linear_workspace(int32_t T, int64_t n, int64_t k) { return ss_w4a16_linear_workspace(T, n, k); }
 
-ss_status ss_w4a16_linear(const void* x_bf16, int32_t T, const void* qweight, const void* scale,
-                          const void* zero, int64_t n, int64_t k, void* y_bf16, float* y_f32,
-                          void* workspace, size_t ws_bytes, void* stream) {
-  const char* fn = __func__;
-  ss_status s = linear_common(fn, x_bf16, T, n, k, y_bf16, y_f32, workspace, ws_bytes);
+static ss_status w4_linear(const char* fn, const void* x, int32_t T, const ss_linear& w, int64_t n, int64_t k,
+                           void* y_bf16, float* y_f32, void* ws, size_t ws_bytes, void* stream) {
+  ss_status s = linear_sizes(fn, T, n, k);
   if (s != SS_OK) return s;
-  REQ_PTR(qweight, 16); REQ_PTR(scale, 4); REQ_PTR(zero, 4);
+  const ss::W4Plan pl = ss::plan_w4(T, (int)n, (int)k, ss::EPI_STORE, 0, true);
+  if ((s = linear_common(fn, x, T, n, k, y_bf16, y_f32, ws, ws_bytes, pl.ws_bytes)) != SS_OK) return s;
+  if ((s = check_linear(fn, w, "weight")) != SS_OK) return s;
   if ((s = check_device(fn)) != SS_OK) return s;
-  ss_linear w{SS_W4G64, qweight, scale, zero, nullptr};
-  ss::GemmArgs a = gemm_args(x_bf16, T, w, (int)n, (int)k);
+  ss::W4Args a = w4_args(x, T, w, (int)n, (int)k);
   a.epi = ss::EPI_STORE;
   a.y_f32 = y_f32;
   a.y_bf16 = static_cast<uint16_t*>(y_bf16);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return launched(fn, ss::launch_gemm(a, ss::plan_gemm(T, (int)n, (int)k, ss::EPI_STORE, 0), workspace, st), st);
+  return launched(fn, ss::launch_w4(a, pl, ws, st), st);
 }
 
-size_t ss_w4a16_gate_up_swiglu_workspace(int32_t T, int64_t I, int64_t k) {
-  if (T < 1 || I <= 0 || k < 128) return 0;
-  return ss::plan_gemm(T, (int)(2 * I), (int)k, ss::EPI_SWIGLU, (int)I).ws_bytes;
+ss_status ss_w4a16_linear(const void* x_bf16, int32_t T, const void* qweight, const void* scale,
+                          const void* zero, int64_t n, int64_t k, void* y_bf16, float* y_f32,
+                          void* workspace, size_t ws_bytes, void* stream) {
+  const ss_linear w{SS_W4G64, qweight, scale, zero, nullptr};
+  return w4_linear(__func__, x_bf16, T, w, n, k, y_bf16, y_f32, workspace, ws_bytes, stream);
 }
 
-ss_status ss_w4a16_gate_up_swiglu(const void* x_bf16, int32_t T, const void* qweight, const void* scale,
-                                  const void* zero, int64_t I, int64_t k, void* u_bf16, void* workspace,
-                                  size_t ws_bytes, void* stream) {
-  const char* fn = __func__;
+static ss_status w4_gate_up(const char* fn, const void* x, int32_t T, const ss_linear& w, int64_t I, int64_t k,
+                            void* u_bf16, void* ws, size_t ws_bytes, void* stream) {
   if (T < 1 || T > 256) return fail(SS_ERR_UNSUPPORTED, "%s: T must be in 1..256 (got %d)", fn, T);
   if (I <= 0 || k <= 0) return fail(SS_ERR_INVALID_ARG, "%s: I and k must be positive", fn);
   if (k % 128) return fail(SS_ERR_UNSUPPORTED, "%s: k must be a multiple of 128", fn);
   if (I % 16) return fail(SS_ERR_UNSUPPORTED, "%s: I must be a multiple of 16", fn);
   if (2 * I > 0x7FFFFFFF / 256 || k > 0x7FFFFFFF / 2) return fail(SS_ERR_UNSUPPORTED, "%s: I or k too large", fn);
-  REQ_PTR(x_bf16, 16); REQ_PTR(qweight, 16); REQ_PTR(scale, 4); REQ_PTR(zero, 4); REQ_PTR(u_bf16, 2);
-  const ss::GemmPlan pl = ss::plan_gemm(T, (int)(2 * I), (int)k, ss::EPI_SWIGLU, (int)I);
-  if (pl.ws_bytes > 0 && (!workspace || ws_bytes < pl.ws_bytes))
-    return fail(SS_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, pl.ws_bytes,
-                workspace ? ws_bytes : 0);
-  OPT_PTR(workspace, 16);
-  ss_status s = check_device(fn);
+  REQ_PTR(x, 16); REQ_PTR(u_bf16, 2);
+  ss_status s = check_linear(fn, w, "weight");
   if (s != SS_OK) return s;
-  ss_linear w{SS_W4G64, qweight, scale, zero, nullptr};
-  ss::GemmArgs a = gemm_args(x_bf16, T, w, (int)(2 * I), (int)k);
+  const ss::W4Plan pl = ss::plan_w4(T, (int)(2 * I), (int)k, ss::EPI_SWIGLU, (int)I, true);
+  if (pl.ws_bytes > 0 && (!ws || ws_bytes < pl.ws_bytes))
+    return fail(SS_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, pl.ws_bytes, ws ? ws_bytes : 0);
+  OPT_PTR(ws, 16);
+  if ((s = check_device(fn)) != SS_OK) return s;
+  ss::W4Args a = w4_args(x, T, w, (int)(2 * I), (int)k);
   a.epi = ss::EPI_SWIGLU;
   a.swiglu_I = (int)I;
   a.u_bf16 = static_cast<uint16_t*>(u_bf16);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return launched(fn, ss::launch_gemm(a, pl, workspace, st), st);
+  return launched(fn, ss::launch_w4(a, pl, ws, st), st);
+}
+
+size_t ss_w4a16_gate_up_swiglu_workspace(int32_t T, int64_t I, int64_t k) {
+  if (T < 1 || T > 256 || I <= 0 || I % 16 || k < 128 || k % 128 || 2 * I > 0x7FFFFFFF / 256) return 0;
+  return ss::plan_w4(T, (int)(2 * I), (int)k, ss::EPI_SWIGLU, (int)I, true).ws_bytes;
+}
+
+ss_status ss_w4a16_gate_up_swiglu(const void* x_bf16, int32_t T, const void* qweight, const void* scale,
+                                  const void* zero, int64_t I, int64_t k, void* u_bf16, void* workspace,
+                                  size_t ws_bytes, void* stream) {
+  const ss_linear w{SS_W4G64, qweight, scale, zero, nullptr};
+  return w4_gate_up(__func__, x_bf16, T, w, I, k, u_bf16, workspace, ws_bytes, stream);
 }
 
 size_t ss_w4_tiled_bytes(int64_t n, int64_t k) {
@@ -362,59 +405,33 @@ ss_status ss_w4_tile(const void* qweight, const void* scale, const void* zero, i
 
 ss_status ss_w4a16_linear_tiled(const void* x_bf16, int32_t T, const void* tiled, int64_t n, int64_t k,
                                 void* y_bf16, float* y_f32, void* workspace, size_t ws_bytes, void* stream) {
-  const char* fn = __func__;
-  ss_status s = linear_common(fn, x_bf16, T, n, k, y_bf16, y_f32, workspace, ws_bytes);
-  if (s != SS_OK) return s;
-  REQ_PTR(tiled, 16);
-  if ((s = check_device(fn)) != SS_OK) return s;
-  ss_linear w{SS_W4G64_TILED, tiled, nullptr, nullptr, nullptr};
-  ss::GemmArgs a = gemm_args(x_bf16, T, w, (int)n, (int)k);
-  a.epi = ss::EPI_STORE;
-  a.y_f32 = y_f32;
-  a.y_bf16 = static_cast<uint16_t*>(y_bf16);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  return launched(fn, ss::launch_gemm(a, ss::plan_gemm(T, (int)n, (int)k, ss::EPI_STORE, 0), workspace, st), st);
+  const ss_linear w{SS_W4G64_TILED, tiled, nullptr, nullptr, nullptr};
+  return w4_linear(__func__, x_bf16, T, w, n, k, y_bf16, y_f32, workspace, ws_bytes, stream);
 }
 
 ss_status ss_w4a16_gate_up_swiglu_tiled(const void* x_bf16, int32_t T, const void* tiled, int64_t I, int64_t k,
                                         void* u_bf16, void* workspace, size_t ws_bytes, void* stream) {
-  const char* fn = __func__;
-  if (T < 1 || T > 256) return fail(SS_ERR_UNSUPPORTED, "%s: T must be in 1..256 (got %d)", fn, T);
-  if (I <= 0 || k <= 0) return fail(SS_ERR_INVALID_ARG, "%s: I and k must be positive", fn);
-  if (k % 128) return fail(SS_ERR_UNSUPPORTED, "%s: k must be a multiple of 128", fn);
-  if (I % 16) return fail(SS_ERR_UNSUPPORTED, "%s: I must be a multiple of 16", fn);
-  if (2 * I > 0x7FFFFFFF / 256 || k > 0x7FFFFFFF / 2) return fail(SS_ERR_UNSUPPORTED, "%s: I or k too large", fn);
-  REQ_PTR(x_bf16, 16); REQ_PTR(tiled, 16); REQ_PTR(u_bf16, 2);
-  const ss::GemmPlan pl = ss::plan_gemm(T, (int)(2 * I), (int)k, ss::EPI_SWIGLU, (int)I);
-  if (pl.ws_bytes > 0 && (!workspace || ws_bytes < pl.ws_bytes))
-    return fail(SS_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, pl.ws_bytes,
-                workspace ? ws_bytes : 0);
-  OPT_PTR(workspace, 16);
-  ss_status s = check_device(fn);
-  if (s != SS_OK) return s;
-  ss_linear w{SS_W4G64_TILED, tiled, nullptr, nullptr, nullptr};
-  ss::GemmArgs a = gemm_args(x_bf16, T, w, (int)(2 * I), (int)k);
-  a.epi = ss::EPI_SWIGLU;
-  a.swiglu_I = (int)I;
-  a.u_bf16 = static_cast<uint16_t*>(u_bf16);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  return launched(fn, ss::launch_gemm(a, pl, workspace, st), st);
+  const ss_linear w{SS_W4G64_TILED, tiled, nullptr, nullptr, nullptr};
+  return w4_gate_up(__func__, x_bf16, T, w, I, k, u_bf16, workspace, ws_bytes, stream);
 }
 
 ss_status ss_bf16_linear(const void* x_bf16, int32_t T, const void* w_bf16, int64_t n, int64_t k,
                          void* y_bf16, float* y_f32, void* workspace, size_t ws_bytes, void* stream) {
   const char* fn = __func__;
-  ss_status s = linear_common(fn, x_bf16, T, n, k, y_bf16, y_f32, workspace, ws_bytes);
+  ss_status s = linear_sizes(fn, T, n, k);
   if (s != SS_OK) return s;
+  const ss::GemmPlan pl = ss::plan_gemm(T, (int)n, (int)k, ss::EPI_STORE, 0);
+  if ((s = linear_common(fn, x_bf16, T, n, k, y_bf16, y_f32, workspace, ws_bytes, pl.ws_bytes)) != SS_OK) return s;
   REQ_PTR(w_bf16, 16);
   if ((s = check_device(fn)) != SS_OK) return s;
-  ss_linear w{SS_BF16, nullptr, nullptr, nullptr, w_bf16};
-  ss::GemmArgs a = gemm_args(x_bf16, T, w, (int)n, (int)k);
+  ss::GemmArgs a = bf16_args(x_bf16, T, w_bf16, (int)n, (int)k);
   a.epi = ss::EPI_STORE;
   a.y_f32 = y_f32;
   a.y_bf16 = static_cast<uint16_t*>(y_bf16);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return launched(fn, ss::launch_gemm(a, ss::plan_gemm(T, (int)n, (int)k, ss::EPI_STORE, 0), workspace, st), st);
+  s = launched(fn, ss::launch_gemm(a, pl, workspace, st), st);
+  if (s != SS_OK) return s;
+  return check_bf16_waits(fn);
 }
 
 // ------------------------------------------------------------------ tree
@@ -597,29 +614,31 @@ ss_status ss_draft_tree_step(const ss_model* m, const ss_step_args* a, void* wor
     // 0, then the residual GEMMs' epilogues and resid_finish); the consumer GEMM scales its
     // output rows by 1 / rms.
     if (l == 0) RUN(ss::launch_row_stats(Ly.h32, T, H, static_cast<const uint16_t*>(ly.norm1), Ly.xn, Ly.ssq, st));
-    auto consume_norm = [&](ss::GemmArgs& g) {
+    auto consume_norm = [&](auto& g) {
       g.ssq_in = Ly.ssq;
       g.ssq_n = H / 32;
       g.rms_H = H;
       g.rms_eps = m->rms_eps;
     };
-    auto produce_norm = [&](ss::GemmArgs& g, const void* gain) {
-      if (!gain) return;
-      g.hg_out = Ly.xn;
-      g.hg_gain = static_cast<const uint16_t*>(gain);
-      g.ssq_out = Ly.ssq;
-      g.ssq_n = H / 32;
-    };
-    {
-      ss::GemmArgs g = gemm_args(Ly.xn, T, ly.qkv, qkvN, H);
+    // qkv: int4 on the W4 engine (its K ranges' partials go straight to the RoPE scatter),
+    // bf16 on the bf16 engine (whole output in qkv32)
+    if (is_int4(ly.qkv)) {
+      ss::W4Args g = w4_args(Ly.xn, T, ly.qkv, qkvN, H);
       g.epi = ss::EPI_STORE;
       g.y_f32 = Ly.qkv32;
       g.defer_reduce = true;
       consume_norm(g);
-      const ss::GemmPlan pl = ss::plan_gemm(T, qkvN, H, g.epi, 0);
-      RUN(ss::launch_gemm(g, pl, Ly.gemm_ws, st));
-      RUN(ss::launch_qkv_finish(ss::gemm_split_view(pl, Ly.gemm_ws), Ly.qkv32, Ly.rope, T, nq, nkv, hd,
-                                Ly.qbuf, tk, tv, st));
+      const ss::W4Plan pl = ss::plan_w4(T, qkvN, H, g.epi, 0, false);
+      RUN(ss::launch_w4(g, pl, Ly.gemm_ws, st));
+      RUN(ss::launch_qkv_finish(static_cast<const float*>(Ly.gemm_ws), pl.splits, Ly.qkv32, Ly.rope, T, nq, nkv,
+                                hd, Ly.qbuf, tk, tv, st));
+    } else {
+      ss::GemmArgs g = bf16_args(Ly.xn, T, ly.qkv.w, qkvN, H);
+      g.epi = ss::EPI_STORE;
+      g.y_f32 = Ly.qkv32;
+      consume_norm(g);
+      RUN(ss::launch_gemm(g, ss::plan_gemm(T, qkvN, H, g.epi, 0), Ly.gemm_ws, st));
+      RUN(ss::launch_qkv_finish(nullptr, 1, Ly.qkv32, Ly.rope, T, nq, nkv, hd, Ly.qbuf, tk, tv, st));
     }
     {
       ss::AttnArgs aa{};
@@ -631,47 +650,59 @@ ss_status ss_draft_tree_step(const ss_model* m, const ss_step_args* a, void* wor
       aa.sm_scale = 1.0f / std::sqrt((float)hd);
       RUN(ss::launch_attention(aa, apl, Ly.attn_ws, st));
     }
-    {
-      ss::GemmArgs g = gemm_args(Ly.attn, T, ly.o, H, nq * hd);
+    // residual GEMMs: h += x W^T, then the next RMSNorm's inputs (hg = bf16(h * gain), ssq);
+    // the W4 engine writes them in its epilogue (or its split finish), the bf16 engine
+    // through row_stats
+    auto residual = [&](const ss_linear& w, const void* x, int K, const void* gain) -> hipError_t {
+      hipError_t e2;
+      if (is_int4(w)) {
+        ss::W4Args g = w4_args(x, T, w, H, K);
+        g.epi = ss::EPI_RESID;
+        g.resid = Ly.h32;
+        g.defer_reduce = true;
+        if (gain) {
+          g.hg_out = Ly.xn;
+          g.hg_gain = static_cast<const uint16_t*>(gain);
+          g.ssq_out = Ly.ssq;
+          g.ssq_n = H / 32;
+        }
+        const ss::W4Plan pl = ss::plan_w4(T, H, K, g.epi, 0, false);
+        if ((e2 = ss::launch_w4(g, pl, Ly.gemm_ws, st)) != hipSuccess) return e2;
+        return ss::launch_resid_finish(static_cast<const float*>(Ly.gemm_ws), pl.splits, Ly.h32, T, H,
+                                       static_cast<const uint16_t*>(gain), Ly.xn, Ly.ssq, st);
+      }
+      ss::GemmArgs g = bf16_args(x, T, w.w, H, K);
       g.epi = ss::EPI_RESID;
       g.resid = Ly.h32;
-      g.defer_reduce = true;
-      produce_norm(g, ly.norm2);
-      const ss::GemmPlan pl = ss::plan_gemm(T, H, nq * hd, g.epi, 0);
-      RUN(ss::launch_gemm(g, pl, Ly.gemm_ws, st));
-      // split blocks: residual add + RMSNorm-2 inputs
-      RUN(ss::launch_resid_finish(ss::gemm_split_view(pl, Ly.gemm_ws), pl.sk_blocks, Ly.h32, T, H,
-                                  static_cast<const uint16_t*>(ly.norm2), Ly.xn, Ly.ssq, st));
-    }
-    // MLP block
-    {
-      ss::GemmArgs g = gemm_args(Ly.xn, T, ly.gate_up, 2 * I, H);
+      if ((e2 = ss::launch_gemm(g, ss::plan_gemm(T, H, K, g.epi, 0), Ly.gemm_ws, st)) != hipSuccess) return e2;
+      if (!gain) return hipSuccess;
+      return ss::launch_row_stats(Ly.h32, T, H, static_cast<const uint16_t*>(gain), Ly.xn, Ly.ssq, st);
+    };
+    RUN(residual(ly.o, Ly.attn, nq * hd, ly.norm2));
+    // MLP block: gate_up with SwiGLU (rows scaled by RMSNorm-2), then down
+    if (is_int4(ly.gate_up)) {
+      ss::W4Args g = w4_args(Ly.xn, T, ly.gate_up, 2 * I, H);
+      g.epi = ss::EPI_SWIGLU;
+      g.swiglu_I = I;
+      g.u_bf16 = Ly.ubuf;
+      consume_norm(g);
+      RUN(ss::launch_w4(g, ss::plan_w4(T, 2 * I, H, g.epi, I, true), Ly.gemm_ws, st));
+    } else {
+      ss::GemmArgs g = bf16_args(Ly.xn, T, ly.gate_up.w, 2 * I, H);
       g.epi = ss::EPI_SWIGLU;
       g.swiglu_I = I;
       g.u_bf16 = Ly.ubuf;
       consume_norm(g);
       RUN(ss::launch_gemm(g, ss::plan_gemm(T, 2 * I, H, g.epi, I), Ly.gemm_ws, st));
     }
-    {
-      ss::GemmArgs g = gemm_args(Ly.ubuf, T, ly.down, H, I);
-      g.epi = ss::EPI_RESID;
-      g.resid = Ly.h32;
-      g.defer_reduce = true;
-      // the next layer's RMSNorm-1 inputs (none after the last layer)
-      const void* next_norm = (l + 1 < m->L) ? m->layers[l + 1].norm1 : nullptr;
-      produce_norm(g, next_norm);
-      const ss::GemmPlan pl = ss::plan_gemm(T, H, I, g.epi, 0);
-      RUN(ss::launch_gemm(g, pl, Ly.gemm_ws, st));
-      RUN(ss::launch_resid_finish(ss::gemm_split_view(pl, Ly.gemm_ws), pl.sk_blocks, Ly.h32, T, H,
-                                  static_cast<const uint16_t*>(next_norm), Ly.xn, Ly.ssq, st));
-    }
+    // the next layer's RMSNorm-1 inputs (none after the last layer)
+    RUN(residual(ly.down, Ly.ubuf, I, (l + 1 < m->L) ? m->layers[l + 1].norm1 : nullptr));
   }
   if (a->hidden_out) RUN(ss::launch_f32_to_bf16(Ly.h32, (size_t)T * H, static_cast<uint16_t*>(a->hidden_out), st));
   if (a->logits) {
     RUN(ss::launch_rmsnorm(Ly.h32, static_cast<const uint16_t*>(m->final_norm), R, H, m->rms_eps, Ly.xn,
                            a->logit_rows, T, Ly.err, st));
-    ss_linear head{SS_BF16, nullptr, nullptr, nullptr, m->lm_head};
-    ss::GemmArgs g = gemm_args(Ly.xn, R, head, m->V, H);
+    ss::GemmArgs g = bf16_args(Ly.xn, R, m->lm_head, m->V, H);
     g.epi = ss::EPI_STORE;
     g.y_f32 = a->logits;
     RUN(ss::launch_gemm(g, ss::plan_gemm(R, m->V, H, g.epi, 0), Ly.gemm_ws, st));
@@ -679,6 +710,7 @@ ss_status ss_draft_tree_step(const ss_model* m, const ss_step_args* a, void* wor
 #undef RUN
   s = launched(fn, hipSuccess, st);
   if (s != SS_OK) return s;
+  if ((s = check_bf16_waits(fn)) != SS_OK) return s;
   return check_err_word(fn, Ly.err, st);
 }
 

@@ -15,12 +15,30 @@ enum Epilogue { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
 // the GEMM's lane order followed by 16 rows x 2 groups of (scale, zero) fp16 pairs.
 constexpr int TILE_BLOCK_BYTES = 1024 + 16 * 2 * 4;
 
-struct GemmArgs {
+// ------------------------------------------------------------------ W4A16 GEMM (gemm_w4.hip)
+
+// Decomposition of one int4 GEMM: units = token blocks x tile groups x K ranges; a unit is
+// one workgroup's job. Split K ranges leave fp32 partials [splits][T][nout] in the
+// workspace, added in range order by the consumer or by the reduce kernel.
+struct W4Plan {
+  int TT;          // 16-token tiles per token block (1..4)
+  int tb_count;    // token blocks of 64
+  int nch;         // 128-wide K chunks
+  int NL;          // logical tiles: 32 rows (SwiGLU: 16 gate rows + their 16 up rows)
+  int nout;        // columns of a partial slice: N, or 2 I for SwiGLU
+  int n_groups, splits, units, G;
+  size_t ws_bytes; // partials (0 when K is not split)
+};
+// reduce_launch: the GEMM adds its own K ranges (no consumer does it)
+W4Plan plan_w4(int T, int N, int K, int epi, int swiglu_I, bool reduce_launch);
+int w4_tpw_max(int TT, int epi);
+
+struct W4Args {
   const uint16_t* x;   // bf16 [T][K]
-  const uint8_t* qw;   // int4 weights, or null for bf16 weights
-  const uint16_t* sc;
+  const uint8_t* qw;   // tiled blocks (tiled) or codes [N][K/2]
+  const uint16_t* sc;  // fp16 [N][K/64] (plain layout)
   const uint16_t* zp;
-  const uint16_t* wb;  // bf16 weights when qw is null
+  bool tiled;
   int T, N, K;
   int epi;
   int swiglu_I;
@@ -28,59 +46,71 @@ struct GemmArgs {
   uint16_t* y_bf16;
   float* resid;
   uint16_t* u_bf16;
-  bool defer_reduce;   // leave split blocks' partials for the consumer (see SplitView)
-  bool tiled;          // qw holds the tiled layout (TILE_BLOCK_BYTES per tile and chunk)
+  bool defer_reduce;   // split K ranges: leave the partials to the consumer
   // RMSNorm folded into a consumer GEMM: x = bf16(h * gain), outputs of token row t scaled
   // by 1 / sqrt(sum(ssq_in[t][0 .. ssq_n)) / rms_H + rms_eps)
   const float* ssq_in;
   int ssq_n, rms_H;
   float rms_eps;
-  // RMSNorm inputs written by an EPI_RESID GEMM for its whole blocks (split blocks: by
-  // launch_resid_finish): hg_out = bf16(h * hg_gain), ssq_out[t][n / 32] (ssq_n groups)
+  // RMSNorm inputs written by an EPI_RESID GEMM without K split: hg_out = bf16(h * hg_gain),
+  // ssq_out[t][n / 32] (ssq_n groups)
   uint16_t* hg_out;
   const uint16_t* hg_gain;
   float* ssq_out;
 };
+hipError_t launch_w4(const W4Args& a, const W4Plan& pl, void* ws, hipStream_t st);
 
-// Decomposition of one GEMM call: row blocks x token blocks, each cut into steps of KS
-// 128-wide K chunks; whole blocks first (dp_rounds per workgroup), the rest split
-// evenly (stream-K) over G_sk workgroups.
+// ------------------------------------------------------------------ bf16-weight GEMM (gemm_bf16.hip)
+
+struct GemmArgs {
+  const uint16_t* x;   // bf16 [T][K]
+  const uint16_t* wb;  // bf16 weights [N][K]
+  int T, N, K;
+  int epi;
+  int swiglu_I;
+  float* y_f32;
+  uint16_t* y_bf16;
+  float* resid;
+  uint16_t* u_bf16;
+  const float* ssq_in;   // folded RMSNorm, as W4Args
+  int ssq_n, rms_H;
+  float rms_eps;
+};
+
+// Decomposition of one bf16 GEMM call: row blocks x token blocks, each cut into 128-wide
+// K chunks; whole blocks first (dp_rounds per workgroup), the rest split evenly (stream-K)
+// over G_sk workgroups whose partials a reduce kernel adds in K order.
 struct GemmPlan {
-  int KS, TT;
+  int TT;
   int rb_count, tb_count, nchunks, nsteps;
   int G, dp_rounds, sk_first, sk_blocks, G_sk;
   long long sk_units;
-  size_t ws_bytes;         // partials of split blocks (0 when no block is split)
+  size_t ws_bytes;
 };
-
 GemmPlan plan_gemm(int T, int N, int K, int epi, int swiglu_I);
 hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& pl, void* ws, hipStream_t st);
+// the bf16 GEMM's hand-off waits give up after a bound; a set flag means that happened
+// (a pipeline fault: results of that launch are invalid). Cleared by the read.
+hipError_t gemm_bf16_wait_expired(int* expired);
 
-// Where a GEMM launched with defer_reduce left its split blocks' partials (device-side
-// accessors in split_view.h). Non-SwiGLU epilogues only.
-struct SplitView {
-  const float* partials;
-  int RG, TT, tb_count, rows_per_block, rb_count, nsteps, G_sk, sk_first;
-  long long sk_units;
-};
-SplitView gemm_split_view(const GemmPlan& pl, const void* ws);
+// ------------------------------------------------------------------ layer glue (misc.hip)
 
-// Finish a deferred residual GEMM and normalize: for every token row t, h32[t] += the
-// split blocks' sums, then xn[t] = bf16(h32[t] * rsqrt(mean(h32[t]^2) + eps) * gain) when
-// gain is not null. H <= 8192.
-hipError_t launch_resid_finish(const SplitView& v, int sk_blocks, float* h32, int T, int H,
-                               const uint16_t* gain, uint16_t* hg, float* ssq, hipStream_t st);
+// Finish a residual GEMM whose K was split: h32[t][n] += sum over splits of part[s][t][n]
+// (range order), then, with a gain, the next RMSNorm's inputs hg = bf16(h32 * gain) and
+// ssq[t][n / 32] (sums of h^2 per 32 columns). H % 32 == 0.
+hipError_t launch_resid_finish(const float* part, int splits, float* h32, int T, int H, const uint16_t* gain,
+                               uint16_t* hg, float* ssq, hipStream_t st);
 hipError_t launch_row_stats(const float* h32, int T, int H, const uint16_t* gain, uint16_t* hg, float* ssq,
                             hipStream_t st);
 // RoPE angles of one step: rope[t][i] = (cos, sin) of (C + depth[t]) theta^(-2i/hd) for
 // i < hd/2, evaluated in fp64 and rounded to fp32 (all layers share them).
 hipError_t launch_rope_table(const int32_t* depth, int T, int C, int hd, float theta, float2* rope,
                              hipStream_t st);
-// Finish a deferred qkv GEMM (values of unsplit blocks are read from qkv32), apply RoPE
-// from the step's table to the q and k heads and scatter to q [T][nq][hd] and tree K / V
+// qkv values v[t][n] = sum over splits of part[s][t][n] (splits > 1) or qkv32[t][n]; RoPE
+// from the step's table on the q and k heads, scatter to q [T][nq][hd] and tree K / V
 // [nkv][T][hd] (bf16).
-hipError_t launch_qkv_finish(const SplitView& v, const float* qkv32, const float2* rope, int T, int nq, int nkv,
-                             int hd, uint16_t* q, uint16_t* kt, uint16_t* vt, hipStream_t st);
+hipError_t launch_qkv_finish(const float* part, int splits, const float* qkv32, const float2* rope, int T,
+                             int nq, int nkv, int hd, uint16_t* q, uint16_t* kt, uint16_t* vt, hipStream_t st);
 
 // quantization
 hipError_t launch_quantize_g64(const uint16_t* w, int64_t n, int64_t k, uint8_t* q, uint16_t* s,

@@ -9,7 +9,6 @@
 // (Review §6.3); read as Gumbel-top-k sampling without replacement.
 #include "common.h"
 #include "kernels.h"
-#include "split_view.h"
 
 #include <algorithm>
 
@@ -95,63 +94,42 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
 }
 
 
-// ------------------------------------------------------------------ fused split finish
+// ------------------------------------------------------------------ split-K finish
 
-// Residual GEMM, split blocks: workgroup (sb, rg, tt) finishes the 32 rows of row group
-// rg of split block sk_first + sb for the 16 tokens of token tile tt (512 elements, two
-// per thread): h += the pieces' partials in K order, h32 updated and, with a gain, the
-// next RMSNorm's inputs: hg = bf16(h * gain) and ssq[t][n / 32], the group's sum of h^2
-// (the 16 rows j across lanes, the two tiles in each thread). Blocks the GEMM finished
-// itself (one owner) are skipped: their epilogue wrote the same outputs.
-template <int TT>
-__global__ __launch_bounds__(256) void resid_finish_kernel(SplitView v, float* __restrict__ h32, int T, int H,
+// Residual GEMM whose K was split into ranges: thread (token blockIdx.y, column n) adds the
+// ranges' partials in range order (a fixed order) to h32, and with a gain writes the next
+// RMSNorm's inputs: hg = bf16(h * gain) and ssq[t][n / 32], the 32-column group's sum of
+// h^2 (the group's 32 lanes, fixed xor tree).
+__global__ __launch_bounds__(256) void resid_finish_kernel(const float* __restrict__ part, int splits, int T,
+                                                           int H, float* __restrict__ h32,
                                                            const uint16_t* __restrict__ gain,
                                                            uint16_t* __restrict__ hg, float* __restrict__ ssq) {
-  const int sb = blockIdx.x, rg = blockIdx.y, tt = blockIdx.z;
-  const int b = v.sk_first + sb;
-  const SvBlock blk = sv_block(v, b);
-  if (blk.g0 == blk.g1) return;
-  const int tb = b % v.tb_count, rb = b / v.tb_count;
-  const int lane = threadIdx.x & 63, e = threadIdx.x >> 6;
-  const int j = lane & 15, bq = lane >> 4;
-  const int tok = tb * 64 + tt * 16 + 4 * bq + e;
-  const size_t se = (size_t)v.RG * 2 * v.TT * 256;   // floats per partial slot
-  const int np = blk.g1 - blk.g0 + 1;
-  float ss = 0.f;
+  const int tok = blockIdx.y;
+  const int n = blockIdx.x * 256 + threadIdx.x;   // H % 32 == 0: a 32-lane group is all in or all out
+  if (n >= H) return;
+  const size_t slice = (size_t)T * H;
+  const float* src = part + (size_t)tok * H + n;
+  float sum = 0.f;
+  for (int s0 = 0; s0 < splits; s0 += 8) {   // eight independent loads in flight, added in order
+    float x[8];
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int n = rb * v.rows_per_block + rg * 32 + r * 16 + j;
-    const size_t off = (size_t)rg * (2 * v.TT * 256) + ((r * v.TT + tt) * 4 + e) * 64 + 16 * bq + j;
-    float sum = 0.f;
-    for (int p0 = 0; p0 < np; p0 += 8) {   // eight independent loads in flight, added in order
-      float x[8];
+    for (int i = 0; i < 8; ++i) x[i] = s0 + i < splits ? src[(size_t)(s0 + i) * slice] : 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int pi = p0 + i;
-        const size_t slot = pi == 0 ? (size_t)blk.slot0 : (size_t)(2 * (blk.g0 + pi));
-        x[i] = pi < np ? v.partials[slot * se + off] : 0.f;
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (p0 + i < np) sum += x[i];
-    }
-    if (tok < T && n < H) {
-      const size_t o = (size_t)tok * H + n;
-      const float h = h32[o] + sum;
-      h32[o] = h;
-      if (gain) {
-        hg[o] = f32_to_bf16(h * bf16_to_f32(gain[n]));
-        ss += h * h;
-      }
-    }
+    for (int i = 0; i < 8; ++i)
+      if (s0 + i < splits) sum += x[i];
   }
+  const size_t o = (size_t)tok * H + n;
+  const float h = h32[o] + sum;
+  h32[o] = h;
   if (!gain) return;
-  ss += __shfl_xor(ss, 1, 16);
-  ss += __shfl_xor(ss, 2, 16);
-  ss += __shfl_xor(ss, 4, 16);
-  ss += __shfl_xor(ss, 8, 16);
-  const int grp = (rb * v.rows_per_block + rg * 32) >> 5;
-  if (j == 0 && tok < T && grp * 32 < H) ssq[(size_t)tok * (H >> 5) + grp] = ss;
+  hg[o] = f32_to_bf16(h * bf16_to_f32(gain[n]));
+  float x = h * h;
+  x += __shfl_xor(x, 1, 32);
+  x += __shfl_xor(x, 2, 32);
+  x += __shfl_xor(x, 4, 32);
+  x += __shfl_xor(x, 8, 32);
+  x += __shfl_xor(x, 16, 32);
+  if ((n & 31) == 0) ssq[(size_t)tok * (H >> 5) + (n >> 5)] = x;
 }
 
 // The first RMSNorm's inputs from h32 (one workgroup per token row): hg = bf16(h * gain)
@@ -190,91 +168,60 @@ __global__ __launch_bounds__(64) void rope_table_kernel(const int32_t* __restric
   rope[(size_t)t * half + i] = float2{(float)cd, (float)sd};
 }
 
-// qkv GEMM output -> q bf16 [T][nq][hd] and tree K / V bf16 [nkv][T][hd], element-parallel.
-// Workgroup (c, pp, tt) takes one RoPE pair of 16-row sub-tiles of the 128-row chunk c
-// (a head spans ds = hd / 16 sub-tiles; row i of a head pairs with row i + hd/2, ds / 2
-// sub-tiles on) for the 16 tokens of token tile tt; thread (e, bq, j) holds row j of both
-// sub-tiles for token 16 tt + 4 bq + e, the GEMM's fragment order, so a wave reads 256
-// contiguous bytes of a partial slot per sub-tile and piece. Which block a sub-tile lies
-// in, its pieces and their slots are the same for the whole workgroup (scalar registers);
-// a split block's value is its pieces' partials summed in K order, any other value is
-// read from qkv32.
-__device__ __forceinline__ float qkv_value(const SplitView& v, const float* __restrict__ qkv32, int W, int tt,
-                                           int n0, int lane_off, int tok, int j) {
-  const SvBlock b = sv_block(v, (tt >> 2) + (n0 / v.rows_per_block) * v.tb_count);
-  if (b.g1 == b.g0) return qkv32[(size_t)tok * W + n0 + j];
-  const int np = b.g1 - b.g0 + 1;
-  const int nn = n0 % v.rows_per_block;
-  const size_t se = (size_t)v.RG * 2 * v.TT * 256;   // floats per partial slot
-  const float* base = v.partials + (nn >> 5) * (2 * v.TT * 256) + ((((nn >> 4) & 1) * v.TT + (tt & 3)) * 4) * 64;
+// qkv GEMM output -> q bf16 [T][nq][hd] and tree K / V bf16 [nkv][T][hd]. Thread (token
+// blockIdx.y, head h, i < hd / 2) takes the pair of columns (h hd + i, h hd + i + hd / 2):
+// each value is the sum of the K ranges' partials in range order (splits > 1) or the
+// GEMM's output; q and k heads are rotated by the step's RoPE table (rotate-half), v heads
+// are copied.
+__device__ __forceinline__ float qkv_value(const float* __restrict__ part, int splits, const float* __restrict__ qkv32,
+                                           int T, int W, int tok, int n) {
+  if (splits <= 1) return qkv32[(size_t)tok * W + n];
+  const size_t slice = (size_t)T * W;
+  const float* src = part + (size_t)tok * W + n;
   float x = 0.f;
-  for (int p0 = 0; p0 < np; p0 += SV_BATCH) {   // independent loads in flight, added in order
-    float y[SV_BATCH];
+  for (int s0 = 0; s0 < splits; s0 += 8) {
+    float y[8];
 #pragma unroll
-    for (int i = 0; i < SV_BATCH; ++i) {
-      const int pi = p0 + i;
-      const size_t slot = pi == 0 ? (size_t)b.slot0 : (size_t)(2 * (b.g0 + pi));
-      y[i] = pi < np ? base[slot * se + lane_off] : 0.f;
-    }
+    for (int i = 0; i < 8; ++i) y[i] = s0 + i < splits ? src[(size_t)(s0 + i) * slice] : 0.f;
 #pragma unroll
-    for (int i = 0; i < SV_BATCH; ++i)
-      if (p0 + i < np) x += y[i];
+    for (int i = 0; i < 8; ++i)
+      if (s0 + i < splits) x += y[i];
   }
   return x;
 }
 
-__global__ __launch_bounds__(256) void qkv_finish_kernel(SplitView v, const float* __restrict__ qkv32,
+__global__ __launch_bounds__(256) void qkv_finish_kernel(const float* __restrict__ part, int splits,
+                                                         const float* __restrict__ qkv32,
                                                          const float2* __restrict__ rope, int T, int nq, int nkv,
                                                          int hd, uint16_t* __restrict__ q, uint16_t* __restrict__ kt,
                                                          uint16_t* __restrict__ vt) {
-  const int c = blockIdx.x >> 2, pp = blockIdx.x & 3, tt = blockIdx.y;
-  const int W = (nq + 2 * nkv) * hd;
-  const int ds = hd >> 4, hs = ds >> 1;
-  const int s0 = (pp / hs) * ds + pp % hs;   // first sub-tile of the pair; its partner is s0 + hs
-  const int n0 = c * 128 + s0 * 16;          // first row of the first sub-tile
-  if (n0 >= W) return;
-  const int lane = threadIdx.x & 63, e = threadIdx.x >> 6;
-  const int j = lane & 15, bq = lane >> 4;
-  const int tok = tt * 16 + 4 * bq + e;
-  if (tok >= T) return;
-  const int lane_off = e * 64 + 16 * bq + j;
-  const int h = n0 / hd, i = n0 - h * hd + j;
+  const int tok = blockIdx.y;
   const int half = hd >> 1;
-  const bool rot = h < nq + nkv;
-  float2 cs{1.f, 0.f};
-  if (rot) cs = rope[(size_t)tok * half + i];
-  const float a = qkv_value(v, qkv32, W, tt, n0, lane_off, tok, j);
-  const float bb = qkv_value(v, qkv32, W, tt, n0 + half, lane_off, tok, j);
-  if (!rot) {   // value head: no rotation
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  const int heads = nq + 2 * nkv;
+  if (idx >= heads * half) return;
+  const int h = idx / half, i = idx - h * half;
+  const int W = heads * hd;
+  const float a = qkv_value(part, splits, qkv32, T, W, tok, h * hd + i);
+  const float bb = qkv_value(part, splits, qkv32, T, W, tok, h * hd + i + half);
+  if (h >= nq + nkv) {   // value head: no rotation
     uint16_t* dst = vt + ((size_t)(h - nq - nkv) * T + tok) * hd;
     dst[i] = f32_to_bf16(a);
     dst[i + half] = f32_to_bf16(bb);
     return;
   }
+  const float2 cs = rope[(size_t)tok * half + i];
   uint16_t* dst = (h < nq) ? q + ((size_t)tok * nq + h) * hd : kt + ((size_t)(h - nq) * T + tok) * hd;
   dst[i] = f32_to_bf16(a * cs.x - bb * cs.y);
   dst[i + half] = f32_to_bf16(bb * cs.x + a * cs.y);
 }
 
-namespace {
-// the kernels' 32-bit ownership arithmetic
-bool sv_fits(const SplitView& v) {
-  return v.sk_units * (long long)std::max(v.G_sk, 1) < (1LL << 31) && v.nsteps > 0;
-}
-}  // namespace
-
-hipError_t launch_resid_finish(const SplitView& v, int sk_blocks, float* h32, int T, int H,
-                               const uint16_t* gain, uint16_t* hg, float* ssq, hipStream_t st) {
-  if (sk_blocks == 0) return hipSuccess;
-  if (!sv_fits(v) || v.rows_per_block != v.RG * 32 || (H & 31) || (gain && (!hg || !ssq)))
-    return hipErrorInvalidValue;
-  const dim3 grid(sk_blocks, v.RG, v.TT);
-  switch (v.TT) {
-    case 1: hipLaunchKernelGGL(resid_finish_kernel<1>, grid, dim3(256), 0, st, v, h32, T, H, gain, hg, ssq); break;
-    case 2: hipLaunchKernelGGL(resid_finish_kernel<2>, grid, dim3(256), 0, st, v, h32, T, H, gain, hg, ssq); break;
-    case 3: hipLaunchKernelGGL(resid_finish_kernel<3>, grid, dim3(256), 0, st, v, h32, T, H, gain, hg, ssq); break;
-    default: hipLaunchKernelGGL(resid_finish_kernel<4>, grid, dim3(256), 0, st, v, h32, T, H, gain, hg, ssq); break;
-  }
+hipError_t launch_resid_finish(const float* part, int splits, float* h32, int T, int H, const uint16_t* gain,
+                               uint16_t* hg, float* ssq, hipStream_t st) {
+  if (splits <= 1) return hipSuccess;
+  if (!part || (H & 31) || (gain && (!hg || !ssq))) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(resid_finish_kernel, dim3((H + 255) / 256, T), dim3(256), 0, st, part, splits, T, H, h32, gain,
+                     hg, ssq);
   return hipGetLastError();
 }
 
@@ -292,12 +239,12 @@ hipError_t launch_rope_table(const int32_t* depth, int T, int C, int hd, float t
   return hipGetLastError();
 }
 
-hipError_t launch_qkv_finish(const SplitView& v, const float* qkv32, const float2* rope, int T, int nq, int nkv,
-                             int hd, uint16_t* q, uint16_t* kt, uint16_t* vt, hipStream_t st) {
-  const int W = (nq + 2 * nkv) * hd;
-  if ((hd != 64 && hd != 128) || !sv_fits(v) || v.rows_per_block % 16) return hipErrorInvalidValue;
-  const dim3 grid(4 * ((W + 127) / 128), (T + 15) / 16);
-  hipLaunchKernelGGL(qkv_finish_kernel, grid, dim3(256), 0, st, v, qkv32, rope, T, nq, nkv, hd, q, kt, vt);
+hipError_t launch_qkv_finish(const float* part, int splits, const float* qkv32, const float2* rope, int T,
+                             int nq, int nkv, int hd, uint16_t* q, uint16_t* kt, uint16_t* vt, hipStream_t st) {
+  if ((hd != 64 && hd != 128) || (splits > 1 ? !part : !qkv32)) return hipErrorInvalidValue;
+  const int pairs = (nq + 2 * nkv) * (hd / 2);
+  hipLaunchKernelGGL(qkv_finish_kernel, dim3((pairs + 255) / 256, T), dim3(256), 0, st, part, splits, qkv32, rope, T,
+                     nq, nkv, hd, q, kt, vt);
   return hipGetLastError();
 }
 

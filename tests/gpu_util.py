@@ -47,6 +47,11 @@ def assert_close(got, ref, rel_l2=1e-2, max_abs=2e-2, scale_abs=False, bf16_out=
     lim = max_abs * (max(1.0, float(np.sqrt(np.mean(ref ** 2)))) if scale_abs else 1.0)
     bound = lim + (bf16_half_ulp(ref) if bf16_out else 0.0)
     excess = np.max(np.abs(err) - bound) if err.size else 0.0
+    if bf16_out:
+        # the margin without the storage allowance, so the allowance's need stays on record
+        bare = np.max(np.abs(err) - lim) if err.size else 0.0
+        print(f"MARGIN {what}: rel-L2 {rl2:.3e}, max-abs {mab:.3e}, limit {lim:.3e}, "
+              f"excess without the half-ulp allowance {bare:.3e}, with it {excess:.3e}", flush=True)
     assert rl2 <= rel_l2 and excess <= 0, (
         f"{what}: rel-L2 {rl2:.3e} (<= {rel_l2}), max-abs {mab:.3e} (<= {lim:.3e}"
         f"{' + half bf16 ulp' if bf16_out else ''}; worst excess {excess:.3e})")
