@@ -169,7 +169,7 @@ ss_status check_linear(const char* fn, const ss_linear& w, const char* name) {
 
 struct StepLayout {
   int32_t* err;
-  float* ssq;        // [T][H / 32] sums of h^2 per 32-column group (RMSNorm folded into GEMMs)
+  float* ssq;        // [T][ssq_groups(H)] sums of h^2 per 256-column group (RMSNorm folded into GEMMs)
   uint64_t* mask;
   int32_t* depth;
   float2* rope;      // [T][hd / 2] (cos, sin) of the step's RoPE angles
@@ -191,7 +191,7 @@ StepLayout plan_step(const ss_model* m, int T, int C, int R, void* base) {
   const int qkvN = (m->nq + 2 * m->nkv) * m->hd;
   const int rows_norm = std::max(T, R);
   L.err = bp.take<int32_t>(4);
-  L.ssq = bp.take<float>((size_t)T * (m->H / 32));
+  L.ssq = bp.take<float>((size_t)T * ss::ssq_groups(m->H));
   L.mask = bp.take<uint64_t>((size_t)T * W);
   L.depth = bp.take<int32_t>(T);
   L.rope = bp.take<float2>((size_t)T * (m->hd / 2));
@@ -610,13 +610,13 @@ ss_status ss_draft_tree_step(const ss_model* m, const ss_step_args* a, void* wor
     uint16_t* tk = static_cast<uint16_t*>(a->tree_k[l]);
     uint16_t* tv = static_cast<uint16_t*>(a->tree_v[l]);
     // RMSNorm is folded into the GEMM that consumes it: xn holds bf16(h * gain) and ssq the
-    // sums of h^2 per 32-column group, written by whoever finished h (row_stats for layer
-    // 0, then the residual GEMMs' epilogues and resid_finish); the consumer GEMM scales its
-    // output rows by 1 / rms.
+    // sums of h^2 per 256-column group, written by whoever finished h (row_stats for layer
+    // 0, then resid_finish after the residual GEMMs); the consumer GEMM scales its output
+    // rows by 1 / rms.
     if (l == 0) RUN(ss::launch_row_stats(Ly.h32, T, H, static_cast<const uint16_t*>(ly.norm1), Ly.xn, Ly.ssq, st));
     auto consume_norm = [&](auto& g) {
       g.ssq_in = Ly.ssq;
-      g.ssq_n = H / 32;
+      g.ssq_n = ss::ssq_groups(H);
       g.rms_H = H;
       g.rms_eps = m->rms_eps;
     };
@@ -650,9 +650,8 @@ ss_status ss_draft_tree_step(const ss_model* m, const ss_step_args* a, void* wor
       aa.sm_scale = 1.0f / std::sqrt((float)hd);
       RUN(ss::launch_attention(aa, apl, Ly.attn_ws, st));
     }
-    // residual GEMMs: h += x W^T, then the next RMSNorm's inputs (hg = bf16(h * gain), ssq);
-    // the W4 engine writes them in its epilogue (or its split finish), the bf16 engine
-    // through row_stats
+    // residual GEMMs: h += x W^T, then the next RMSNorm's inputs (hg = bf16(h * gain), ssq)
+    // in resid_finish (which also adds the W4 engine's K ranges) or row_stats
     auto residual = [&](const ss_linear& w, const void* x, int K, const void* gain) -> hipError_t {
       hipError_t e2;
       if (is_int4(w)) {
@@ -660,12 +659,6 @@ ss_status ss_draft_tree_step(const ss_model* m, const ss_step_args* a, void* wor
         g.epi = ss::EPI_RESID;
         g.resid = Ly.h32;
         g.defer_reduce = true;
-        if (gain) {
-          g.hg_out = Ly.xn;
-          g.hg_gain = static_cast<const uint16_t*>(gain);
-          g.ssq_out = Ly.ssq;
-          g.ssq_n = H / 32;
-        }
         const ss::W4Plan pl = ss::plan_w4(T, H, K, g.epi, 0, false);
         if ((e2 = ss::launch_w4(g, pl, Ly.gemm_ws, st)) != hipSuccess) return e2;
         return ss::launch_resid_finish(static_cast<const float*>(Ly.gemm_ws), pl.splits, Ly.h32, T, H,

@@ -531,7 +531,7 @@ GemmPlan plan_gemm(int T, int N, int K, int epi, int swiglu_I) {
 
 hipError_t launch_gemm(const GemmArgs& a, const GemmPlan& pl, void* ws, hipStream_t st) {
   if (!a.wb || a.K % CHUNK_K || a.N % 16) return hipErrorInvalidValue;
-  if (a.ssq_in && ((a.ssq_n & 3) || a.epi == EPI_RESID)) return hipErrorInvalidValue;
+  if (a.ssq_in && (a.ssq_n < 1 || a.epi == EPI_RESID)) return hipErrorInvalidValue;
   if (pl.sk_blocks > 0 && !ws) return hipErrorInvalidValue;
   if (pl.sk_units * (long long)std::max(pl.G_sk, 1) >= (1LL << 62)) return hipErrorInvalidValue;
   GemmParams p{};

@@ -91,18 +91,26 @@ __global__ __launch_bounds__(256) void w4_reduce_kernel(const float* __restrict_
 namespace {
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-// cost model of a plan (seconds): per-CU weight bytes against the per-CU share of HBM
-// bandwidth, weights plus activation re-reads against one CU's load path, partial sums
-// written and read back, and a fixed latency per round of units
+// cost model of a plan (seconds), fitted to per-wave timelines of the kernel on MI355X:
+// a unit is a pipeline fill, S super-chunks and the K-phase reduction plus epilogue. A
+// super-chunk costs the larger of its math (per SIMD: two waves x TPW tiles x 4 k-steps of
+// one 17-instruction dequantization plus TT MFMAs, about 74 + 11.4 TT cycles, plus about
+// 1000 cycles of barrier skew) and its weight bytes at the CU's share of HBM bandwidth.
+// Split K ranges add their fp32 partial sums written and read back, and a reduce launch
+// when no consumer adds them.
 double plan_cost(const W4Plan& pl, int T, int nout, bool reduce_launch) {
-  const double bw_cu = 6.0e12 / MAX_WGS, ta_cu = 64.0 * 2.1e9, bw = 6.0e12;
+  const double clk = 2.3e9, bw = 7.5e12;
+  const int active = std::min(pl.units, MAX_WGS);
   const int rounds = (pl.units + MAX_WGS - 1) / MAX_WGS;
-  const int maxg = (pl.NL + pl.n_groups - 1) / pl.n_groups;
+  const int tpw = (pl.NL + pl.n_groups - 1) / pl.n_groups;
   const int chunks = (pl.nch + pl.splits - 1) / pl.splits;
-  const double w = (double)rounds * maxg * 2 * chunks * TILE_BLOCK_BYTES;
-  const double a = (double)rounds * pl.TT * 16 * chunks * CHK * 2;
-  double t = std::max(w / bw_cu, (w + a) / ta_cu) + rounds * 1.5e-6;
-  if (pl.splits > 1) t += 2.0 * pl.splits * T * (double)nout * 4 / bw + (reduce_launch ? 4e-6 : 0.0);
+  const int S = (chunks + w4::KP - 1) / w4::KP;
+  const double step_math = 1000.0 + 2.0 * tpw * 4 * (74.0 + 11.4 * pl.TT);
+  const double step_mem = (double)w4::KP * 2 * tpw * TILE_BLOCK_BYTES / (bw / active / clk);
+  const double fill = 4000.0 + step_mem;
+  const double epi = 1000.0 + 450.0 * tpw * pl.TT;
+  double t = rounds * (fill + S * std::max(step_math, step_mem) + epi) / clk;
+  if (pl.splits > 1) t += 2.0 * pl.splits * T * (double)nout * 4 / 5.0e12 + (reduce_launch ? 3e-6 : 0.0);
   return t;
 }
 }  // namespace
@@ -114,23 +122,21 @@ W4Plan plan_w4(int T, int N, int K, int epi, int swiglu_I, bool reduce_launch) {
   best.nch = std::max(1, K / CHK);
   best.NL = epi == EPI_SWIGLU ? swiglu_I / 16 : (N + 31) / 32;
   best.nout = epi == EPI_SWIGLU ? 2 * swiglu_I : N;
-  const int tpw = w4_tpw_max(best.TT, epi);
-  const int min_groups = (best.NL + tpw - 1) / tpw;
+  const int tpw_max = w4_tpw_max(best.TT, epi);
   double best_t = 1e30;
   bool found = false;
-  for (int splits = 1; splits <= std::min(best.nch, 64); ++splits) {
-    for (int rounds = 0; rounds <= 8; ++rounds) {
-      // rounds == 0: the fewest groups the registers allow; else the most groups that fit
-      int ng = rounds == 0 ? min_groups : (rounds * MAX_WGS) / (best.tb_count * splits);
-      ng = std::min(std::max(ng, min_groups), best.NL);
-      if (ng < 1) continue;
+  for (int tpw = 1; tpw <= tpw_max; ++tpw) {
+    const int ng = (best.NL + tpw - 1) / tpw;
+    if (tpw > 1 && (best.NL + ng - 1) / ng < tpw) continue;   // the same groups as a smaller tpw
+    for (int splits = 1; splits <= std::min(best.nch, 64); ++splits) {
       W4Plan pl = best;
       pl.splits = splits;
       pl.n_groups = ng;
       pl.units = best.tb_count * ng * splits;
+      if (splits > 1 && (double)splits * T * best.nout * sizeof(float) > 256.0 * (1 << 20)) break;
       const double t = plan_cost(pl, T, best.nout, reduce_launch);
-      // equal cost: more units (every CU streams)
-      if (t < best_t * 0.999 || (t <= best_t * 1.001 && pl.splits == best.splits && pl.units > best.units)) {
+      // equal cost: fewer K splits (less partial-sum traffic)
+      if (t < best_t * 0.999) {
         best_t = t;
         best = pl;
         found = true;
@@ -139,7 +145,7 @@ W4Plan plan_w4(int T, int N, int K, int epi, int swiglu_I, bool reduce_launch) {
   }
   if (!found) {
     best.splits = 1;
-    best.n_groups = std::max(1, min_groups);
+    best.n_groups = (best.NL + tpw_max - 1) / tpw_max;
     best.units = best.tb_count * best.n_groups;
   }
   best.G = std::min(best.units, MAX_WGS);
@@ -158,10 +164,7 @@ hipError_t launch_w4(const W4Args& a, const W4Plan& pl, void* ws, hipStream_t st
     if (maxg < 1 || maxg > w4_tpw_max(pl.TT, a.epi)) return hipErrorInvalidValue;
   }
   if (pl.splits > 1 && !ws) return hipErrorInvalidValue;
-  // producers of RMSNorm inputs write them only where they finish the sums (no K split)
-  if (a.hg_out && (a.epi != EPI_RESID || !a.ssq_out || !a.hg_gain || (pl.splits > 1 && !a.defer_reduce)))
-    return hipErrorInvalidValue;
-  if (a.ssq_in && a.epi == EPI_RESID) return hipErrorInvalidValue;
+  if (a.ssq_in && (a.epi == EPI_RESID || a.ssq_n < 1 || a.ssq_n > w4::SSQ_MAX)) return hipErrorInvalidValue;
   if (pl.splits > 1 && a.epi == EPI_RESID && !a.defer_reduce) return hipErrorInvalidValue;
   W4Params p{};
   p.x = a.x; p.qw = a.qw; p.sc = a.sc; p.zp = a.zp;
@@ -172,8 +175,6 @@ hipError_t launch_w4(const W4Args& a, const W4Plan& pl, void* ws, hipStream_t st
   p.y_f32 = a.y_f32; p.y_bf16 = a.y_bf16; p.resid = a.resid; p.u_bf16 = a.u_bf16;
   p.part = pl.splits > 1 ? static_cast<float*>(ws) : nullptr;
   p.ssq_in = a.ssq_in; p.ssq_n = a.ssq_n; p.rms_H = a.rms_H; p.rms_eps = a.rms_eps;
-  p.hg_out = a.hg_out;
-  p.hg_gain = a.hg_gain; p.ssq_out = a.ssq_out;
   const int maxg = (pl.NL + pl.n_groups - 1) / pl.n_groups;
   switch (pl.TT) {
     case 1: launch_w4_tt1(p, maxg, a.epi, a.tiled, pl.G, st); break;

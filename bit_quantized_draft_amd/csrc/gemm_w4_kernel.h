@@ -15,6 +15,7 @@ constexpr int RGW = 2;          // row groups: two waves per SIMD, each its own 
 constexpr int NWV = KP * RGW;
 constexpr int CHK = 128;        // chunk width (k)
 constexpr int MAX_WGS = 256;    // one workgroup per CU
+constexpr int SSQ_MAX = 32;     // folded RMSNorm: at most 32 partial sums per token (H <= 8192)
 
 // 16-row tiles a wave can hold (= logical tiles of a unit: each row group takes one half of
 // every logical tile): the 256 registers of each of the two waves of a SIMD (accumulation
@@ -42,9 +43,6 @@ struct W4Params {
   const float* ssq_in;  // folded RMSNorm: rows scaled by 1/sqrt(sum ssq_in[t][:] / rms_H + eps)
   int ssq_n, rms_H;
   float rms_eps;
-  uint16_t* hg_out;     // RMSNorm inputs of the next layer (EPI_RESID, splits == 1)
-  const uint16_t* hg_gain;
-  float* ssq_out;
 };
 
 // launchers of the instantiations (one per token-tile count)
@@ -67,11 +65,45 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
   typedef __bf16 b2v __attribute__((ext_vector_type(2)));
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2v){a, b}, b2v));
 }
-// (a & m) | c in one VOP3 instruction (constants in registers: VOP3 takes no literals)
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+// (a & m) | c, one v_and_or_b32: m and c come from opaque_vgpr, so the compiler cannot
+// fold them into literals (a VOP3 instruction takes none; it would split the operation in
+// an AND and an OR)
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) { return (a & m) | c; }
+// a constant in a VGPR whose value the compiler does not know
+__device__ __forceinline__ uint32_t opaque_vgpr(uint32_t v) {
   uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(m), "v"(c));
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(v));
   return r;
+}
+// VALU instructions of one dequant8 (one shift, four and-or, eight fma_mix, four packs)
+constexpr int DQV = 17;
+
+// Issue order for the scheduler over one super-chunk's math (four k-steps): per k-step its
+// share of the pipeline's register loads, the next fragments' LDS reads, the first tile's
+// dequantization, then each MFMA followed by its share of the next tile's dequantization
+// (MFMA and VALU of one wave overlap only when interleaved). The masks are LLVM's
+// scheduling-group classes: 0x2 VALU, 0x8 MFMA, 0x20 VMEM read, 0x100 LDS read. Pipeline
+// list: NA direct-to-LDS loads (inline asm, not counted), then TPW register loads.
+template <int TT, int TPW, int X>
+__device__ __forceinline__ void sched_tiles() {
+  if constexpr (X < TPW * TT) {
+    constexpr int i = X / TT, t = X % TT;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (i + 1 < TPW) __builtin_amdgcn_sched_group_barrier(0x002, DQV / TT + (t < DQV % TT ? 1 : 0), 0);
+    sched_tiles<TT, TPW, X + 1>();
+  }
+}
+template <int TT, int TPW, int NA, int NLA, int M>
+__device__ __forceinline__ void sched_compute() {
+  if constexpr (M < 4) {
+    constexpr int lo = M * NLA / 4, hi = (M + 1) * NLA / 4;
+    constexpr int vlo = lo > NA ? lo : NA, vhi = hi < NA + TPW ? hi : NA + TPW;
+    if constexpr (vhi > vlo) __builtin_amdgcn_sched_group_barrier(0x020, vhi - vlo, 0);
+    if constexpr (M < 3) __builtin_amdgcn_sched_group_barrier(0x100, TT, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, M == 0 ? DQV + 6 * TPW : DQV, 0);
+    sched_tiles<TT, TPW, 0>();
+    sched_compute<TT, TPW, NA, NLA, M + 1>();
+  }
 }
 // Masks and fp16 bases of the dequantization, kept in registers.
 struct DqConst {
@@ -151,7 +183,7 @@ __global__ __launch_bounds__(NWV * 64) void w4k_kernel(W4Params p) {
   // token t stored at position u ^ (t % 16) (no LDS bank conflicts for the fragment reads)
   __shared__ __align__(16) u32x4_t act[2][KP][NTOK][16];
   __shared__ __align__(16) uint32_t szl[NWV][SLOTS][NSZ][2][32];   // scale / zero words, two tiles a load
-  __shared__ float rs_all[256];                                     // folded RMSNorm row scales
+  __shared__ float rs_all[64];                                      // folded RMSNorm scales of a token block
 
   // the wave index is the same for all lanes of a wave: keep it (and all that derives from
   // it: tiles, chunks, branches) in scalar registers
@@ -161,22 +193,11 @@ __global__ __launch_bounds__(NWV * 64) void w4k_kernel(W4Params p) {
   const int nt16 = p.N >> 4;                 // 16-row tiles of the weight
   const int swI16 = p.swiglu_I >> 4;
   DqConst dk;
-  dk.me = 0x000F000Fu;
-  dk.mo = 0x00F000F0u;
-  dk.x1024 = 0x64006400u;
-  dk.x64 = 0x54005400u;
+  dk.me = opaque_vgpr(0x000F000Fu);
+  dk.mo = opaque_vgpr(0x00F000F0u);
+  dk.x1024 = opaque_vgpr(0x64006400u);
+  dk.x64 = opaque_vgpr(0x54005400u);
 
-  if (p.ssq_in) {
-    // one wave per token: lanes add a strided share of the token's partial sums, then a
-    // fixed xor tree (the order does not depend on timing)
-    for (int t = wave; t < p.T; t += NWV) {
-      float s = 0.f;
-      for (int i = lane; i < p.ssq_n; i += 64) s += p.ssq_in[(size_t)t * p.ssq_n + i];
-      s = wave_sum(s);
-      if (lane == 0) rs_all[t] = 1.0f / sqrtf(s / (float)p.rms_H + p.rms_eps);
-    }
-  }
-  wg_barrier();
 
   // per-lane part of the weight addresses (plain layout): row j of a tile, k slice of b
   const uint32_t lane_q = (uint32_t)j * (uint32_t)(p.K >> 1) + (uint32_t)b * 16;
@@ -205,7 +226,6 @@ __global__ __launch_bounds__(NWV * 64) void w4k_kernel(W4Params p) {
       pv[i] = i < cnt && t < nt16;
       pt[i] = pv[i] ? t : (EPI == EPI_SWIGLU ? (rg == 0 ? L0 : swI16 + L0) : min(2 * L0, nt16 - 1));
     }
-    constexpr int NWL = TPW + NSZ;   // weight loads per super-chunk
 
     f32x4_t acc[TPW][TT];
 #pragma unroll
@@ -215,63 +235,81 @@ __global__ __launch_bounds__(NWV * 64) void w4k_kernel(W4Params p) {
 
     u32x4_t wq[SLOTS][TPW];
 
-    // weights of this wave's chunk of super-chunk s (clamped into the unit's range)
-    auto load_w = [&](int s, auto slot_c) {
-      constexpr int q = decltype(slot_c)::value;
-      const int c = min(c0 + min(s, S - 1) * KP + kp, c1 - 1);
+    // wave-uniform bases of the wave's tiles at chunk 0 (scalar registers): tiled, the tile's
+    // first block; plain, its first row of codes
+    const uint8_t* tbase[TPW];
 #pragma unroll
-      for (int i = 0; i < TPW; ++i) {
-        if (TILED) {
-          const uint8_t* blk = uniform_ptr(p.qw + ((size_t)pt[i] * p.nch + c) * TILE_BLOCK_BYTES);
-          wq[q][i] = *reinterpret_cast<const u32x4_t*>(blk + lane * 16);
-        } else {
-          const uint8_t* row = uniform_ptr(p.qw + (size_t)pt[i] * 16 * (size_t)(p.K >> 1) + (size_t)c * 64);
-          wq[q][i] = *reinterpret_cast<const u32x4_t*>(row + lane_q);
-        }
-      }
-      // (scale, zero) words of two tiles straight into LDS in one 4-byte-per-lane load,
-      // lanes 0-31 tile 2 n, 32-63 tile 2 n + 1 (the last load of an odd count repeats).
-      // Tiled: word 2 j + h = (scale | zero << 16) of row j, group 2 c + h. Plain: lane
-      // (r, half, jj) = (l / 32, l / 16 % 2, l % 16) carries the scale (half 0) or zero
-      // (half 1) pair of groups 2 c, 2 c + 1 of row jj.
+    for (int i = 0; i < TPW; ++i)
+      tbase[i] = uniform_ptr(TILED ? p.qw + (size_t)pt[i] * p.nch * TILE_BLOCK_BYTES
+                                   : p.qw + (size_t)pt[i] * 16 * (size_t)(p.K >> 1));
+    // (scale, zero) words of two tiles go straight into LDS in one 4-byte-per-lane load,
+    // lanes 0-31 tile 2 n, 32-63 tile 2 n + 1 (the last load of an odd count repeats).
+    // Tiled: word 2 j + h = (scale | zero << 16) of row j, group 2 c + h. Plain: lane
+    // (r, half, jj) = (l / 32, l / 16 % 2, l % 16) carries the scale (half 0) or zero
+    // (half 1) pair of groups 2 c, 2 c + 1 of row jj. Tiled, per-lane byte offset from the
+    // first tile's base at chunk 0 (signed: a missing tile repeats an earlier one):
+    int szoff[NSZ];
 #pragma unroll
-      for (int n = 0; n < NSZ; ++n) {
-        const int i0 = 2 * n, i1 = min(2 * n + 1, TPW - 1);
-        if (TILED) {
-          const uint8_t* b0 = uniform_ptr(p.qw + ((size_t)pt[i0] * p.nch + c) * TILE_BLOCK_BYTES + 1024);
-          const uint8_t* b1 = uniform_ptr(p.qw + ((size_t)pt[i1] * p.nch + c) * TILE_BLOCK_BYTES + 1024);
-          dma4((lane < 32 ? b0 : b1) + 4 * (lane & 31), &szl[wave][q][n][0][0]);
-        } else {
-          const int half = (lane >> 4) & 1, jj = lane & 15;
-          const size_t row = (size_t)(lane < 32 ? pt[i0] : pt[i1]) * 16 + jj;
-          dma4((half ? p.zp : p.sc) + row * (size_t)(p.K >> 6) + (size_t)c * 2, &szl[wave][q][n][0][0]);
-        }
-      }
-    };
-    // activation rows of super-chunk s into buffer s & 1: per chunk q of the super-chunk,
+    for (int n = 0; n < NSZ; ++n) {
+      const int i0 = 2 * n, i1 = min(2 * n + 1, TPW - 1);
+      szoff[n] = (lane < 32 ? 0 : (int)(tbase[i1] - tbase[i0])) + 1024 + 4 * (lane & 31);
+    }
+    // the loads that keep the pipeline full, in the order they are issued during a
+    // super-chunk's math: NA activation loads of super-chunk s + 1, then the TPW weight
+    // loads and NSZ (scale, zero) loads of super-chunk s + PD
+    constexpr int NA = KP * 4 * TT / NWV;
+    constexpr int NL_ALL = NA + TPW + NSZ;
+    // activation load x of super-chunk s into buffer s & 1: per chunk q of the super-chunk,
     // one 1 KB load per group of 4 tokens (4 rows x 256 contiguous bytes: whole cache
     // lines), 16 TT loads in all, wave w taking loads w, w + 8, ...; lane i of a load
     // carries token 4 g + i / 16, unit (i % 16) ^ (token % 16). A chunk past the unit's
     // range is replaced by its last chunk (never read); padded tokens are clamped copies.
-    auto load_a = [&](int s) {
+    auto load_a1 = [&](int s, int x) {
       const int buf = s & 1;
       const int sc = min(s, S - 1);
-#pragma unroll
-      for (int x = 0; x < KP * 4 * TT / NWV; ++x) {
-        const int l = wave + NWV * x;
-        const int q = l / (4 * TT), g = l % (4 * TT);
-        const int c = min(c0 + sc * KP + q, c1 - 1);
-        const int t = 4 * g + (lane >> 4);
-        const int unit = (lane & 15) ^ (t & 15);
-        const int tok = min(tb * 64 + t, p.T - 1);
-        const uint16_t* src = p.x + (size_t)tok * p.K + (size_t)c * CHK + unit * 8;
-        dma16(src, &act[buf][q][4 * g][0]);
+      const int l = wave + NWV * x;
+      const int q = l / (4 * TT), g = l % (4 * TT);
+      const int c = min(c0 + sc * KP + q, c1 - 1);
+      const int t = 4 * g + (lane >> 4);
+      const int unit = (lane & 15) ^ (t & 15);
+      const int tok = min(tb * 64 + t, p.T - 1);
+      const uint16_t* src = p.x + (size_t)tok * p.K + (size_t)c * CHK + unit * 8;
+      dma16(src, &act[buf][q][4 * g][0]);
+    };
+    // weight load i (i < TPW: codes of tile i; else scale / zero load i - TPW) of this
+    // wave's chunk of super-chunk s (clamped into the unit's range) into slot q
+    auto load_w1 = [&](int s, int i, auto slot_c) {
+      constexpr int q = decltype(slot_c)::value;
+      const int c = min(c0 + min(s, S - 1) * KP + kp, c1 - 1);
+      if (i < TPW) {
+        const uint32_t off = TILED ? (uint32_t)c * TILE_BLOCK_BYTES + lane * 16 : (uint32_t)c * 64 + lane_q;
+        wq[q][i] = *reinterpret_cast<const u32x4_t*>(tbase[i] + off);
+      } else {
+        const int n = i - TPW;
+        if (TILED) {
+          dma4(tbase[2 * n] + (long long)szoff[n] + (size_t)c * TILE_BLOCK_BYTES, &szl[wave][q][n][0][0]);
+        } else {
+          const int half = (lane >> 4) & 1, jj = lane & 15;
+          const size_t row = (size_t)(lane < 32 ? pt[2 * n] : pt[min(2 * n + 1, TPW - 1)]) * 16 + jj;
+          dma4((half ? p.zp : p.sc) + row * (size_t)(p.K >> 6) + (size_t)c * 2, &szl[wave][q][n][0][0]);
+        }
       }
+    };
+    // load y of the pipeline list during super-chunk s's math (slot q of super-chunk s)
+    auto issue = [&](int s, int y, auto slot_c) {
+      constexpr int q = decltype(slot_c)::value;
+      if (y < NA) load_a1(s + 1, y);
+      else load_w1(s + PD, y - NA, std::integral_constant<int, (q + PD) % SLOTS>{});
     };
     auto compute = [&](int s, auto slot_c) {
       constexpr int q = decltype(slot_c)::value;
       const int c = c0 + s * KP + kp;
-      if (c >= c1) return;
+      if (c >= c1) {
+        // no math for this wave in super-chunk s (past the unit's range): loads only
+#pragma unroll
+        for (int y = 0; y < NL_ALL; ++y) issue(s, y, slot_c);
+        return;
+      }
       const int buf = s & 1;
       // scale and the two offsets per tile, once per super-chunk (a missing tile multiplies
       // a duplicate of another tile's data; its sums are never stored)
@@ -305,6 +343,10 @@ __global__ __launch_bounds__(NWV * 64) void w4k_kernel(W4Params p) {
       for (int t = 0; t < TT; ++t) xa[0][t] = frag(0, t);
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
+        // this k-step's share of the pipeline loads (the memory path works on them while
+        // the VALU dequantizes; a burst at the super-chunk start would stall every wave)
+#pragma unroll
+        for (int y = m * NL_ALL / 4; y < (m + 1) * NL_ALL / 4; ++y) issue(s, y, slot_c);
         if (XB == 1 && m > 0) {
 #pragma unroll
           for (int t = 0; t < TT; ++t) xa[m & 1][t] = frag(m, t);
@@ -313,20 +355,18 @@ __global__ __launch_bounds__(NWV * 64) void w4k_kernel(W4Params p) {
 #pragma unroll
           for (int t = 0; t < TT; ++t) xa[(m + 1) & 1][t] = frag(m + 1, t);
         }
-        // the tiles of this k-step, software-pipelined: tile i + 1 is dequantized before
-        // tile i's MFMAs issue, so no MFMA waits on the VALU result it reads. The last tile
-        // slot may be empty (a group one tile smaller than the largest): it is skipped.
+        // the tiles of this k-step, software-pipelined: tile i + 1 is dequantized while
+        // tile i's MFMAs run. Every tile slot is computed (a group one tile smaller than the
+        // largest multiplies a duplicate, never stored), so the k-step is straight-line code
         auto deq = [&](int i) {
           const u32x4_t w = wq[q][i];
           return dequant8(m == 0 ? w.x : m == 1 ? w.y : m == 2 ? w.z : w.w, sf[i], c1k[i], c64[i], dk);
         };
-        const int nlive = cnt < TPW ? TPW - 1 : TPW;   // wave-uniform
         u32x4_t dcur = deq(0);
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
-          if (i >= nlive) break;
           u32x4_t dnext = dcur;
-          if (i + 1 < TPW && i + 1 < nlive) dnext = deq(i + 1);
+          if (i + 1 < TPW) dnext = deq(i + 1);
 #pragma unroll
           for (int t = 0; t < TT; ++t)
             acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[m & 1][t], __builtin_bit_cast(bf16x8_t, dcur),
@@ -334,31 +374,65 @@ __global__ __launch_bounds__(NWV * 64) void w4k_kernel(W4Params p) {
           dcur = dnext;
         }
       }
+#ifndef W4_NO_SCHED
+      // (three or four token tiles: the interleaving costs more registers than the 256 a
+      // wave has, and the MFMAs already keep the VALU work between them)
+      if constexpr (TT <= 2) sched_compute<TT, TPW, NA, NL_ALL, 0>();
+#endif
     };
-    // one super-chunk: wait for its activations and weights, barrier, start the loads of
-    // act(s + 1) and w(s + PD), multiply. The loads issued after act(s) are those of
-    // w(s + PD - 1) (none left outstanding when PD == 1).
+    auto load_a = [&](int s) {
+#pragma unroll
+      for (int x = 0; x < NA; ++x) load_a1(s, x);
+    };
+    auto load_w = [&](int s, auto slot_c) {
+#pragma unroll
+      for (int i = 0; i < TPW + NSZ; ++i) load_w1(s, i, slot_c);
+    };
+    // one super-chunk: wait for its activations and weights, barrier, then its math with
+    // the loads of act(s + 1) and w(s + PD) spread over it. The loads issued after act(s)
+    // are those of w(s + PD - 1) (none left outstanding when PD == 1).
     auto step = [&](int s, auto slot_c) {
-      constexpr int q = decltype(slot_c)::value;
-      if constexpr (PD >= 2) vm_wait_c<NWL>();
+      if constexpr (PD >= 2) vm_wait_c<TPW + NSZ>();
       else vm_wait_c<0>();
       wg_barrier();   // every wave's share of act(s) has landed; buffer (s + 1) & 1 is free
-      load_a(s + 1);
-      load_w(s + PD, std::integral_constant<int, (q + PD) % SLOTS>{});
       compute(s, slot_c);
     };
 
     load_a(0);
     load_w(0, std::integral_constant<int, 0>{});
     if constexpr (PD >= 2) load_w(1, std::integral_constant<int, 1>{});
-    // whole rounds of SLOTS steps (a step past S issues its clamped loads and skips the
-    // math): the loop body is straight-line code for the compiler's wait counts
+    if (p.ssq_in && wave == 0) {
+      // folded RMSNorm scales of the block's 64 tokens, lane = token: the partial sums in
+      // order (fixed), loads issued after the first super-chunks' so their latency hides in
+      // the pipeline fill; read in the epilogue, several barriers later. Loads are of
+      // clamped in-bounds addresses with the unused values selected away (no branch around
+      // a load, which would be waited for before the next is issued).
+      const float* src = p.ssq_in + (size_t)min(tb * 64 + lane, p.T - 1) * p.ssq_n;
+      float sum = 0.f;
+#pragma unroll
+      for (int e0 = 0; e0 < SSQ_MAX; e0 += 8) {
+        if (e0 >= p.ssq_n) break;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = src[min(e0 + e, p.ssq_n - 1)];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum += e0 + e < p.ssq_n ? v[e] : 0.f;
+      }
+      rs_all[lane] = 1.0f / sqrtf(sum / (float)p.rms_H + p.rms_eps);
+    }
+    // rounds of SLOTS steps (the weight slot of a step is a compile-time index); the loads
+    // issued during the last steps for super-chunks past S are clamped re-reads, drained below
     for (int s = 0; s < S; s += SLOTS) {
       step(s, std::integral_constant<int, 0>{});
+      if (s + 1 >= S) break;
       step(s + 1, std::integral_constant<int, 1>{});
-      if constexpr (SLOTS > 2) step(s + 2, std::integral_constant<int, 2 % SLOTS>{});
+      if constexpr (SLOTS > 2) {
+        if (s + 2 >= S) break;
+        step(s + 2, std::integral_constant<int, 2 % SLOTS>{});
+      }
     }
     vm_wait_c<0>();   // the loads past the end have landed before the LDS is reused
+
 
     // ---- K phases added through LDS (the activation buffers are free once every wave
     // has passed this barrier), per row group: (p0 + p2) + (p1 + p3)
@@ -406,7 +480,7 @@ __global__ __launch_bounds__(NWV * 64) void w4k_kernel(W4Params p) {
           f32x4_t v = acc[i][t];
           if (p.ssq_in) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] *= rs_all[min(tb * 64 + t * 16 + 4 * b + e, 255)];
+            for (int e = 0; e < 4; ++e) v[e] *= rs_all[t * 16 + 4 * b + e];
           }
           *fin_at(i, rg, t) = v;
         }
@@ -442,12 +516,10 @@ __global__ __launch_bounds__(NWV * 64) void w4k_kernel(W4Params p) {
           if (tok < p.T) p.u_bf16[(size_t)tok * p.swiglu_I + g] = f32_to_bf16(silu_f32(v0[e]) * v1[e]);
         }
       } else {
-        float ss[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
           if (r == 1 && !has1) continue;
           const int n = 32 * L + 16 * r + j;
-          const float gn = (EPI == EPI_RESID && p.hg_out) ? bf16_to_f32(p.hg_gain[n]) : 0.f;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int tok = tb * 64 + t * 16 + 4 * b + e;
@@ -455,29 +527,11 @@ __global__ __launch_bounds__(NWV * 64) void w4k_kernel(W4Params p) {
             const size_t o = (size_t)tok * p.N + n;
             const float v = r ? v1[e] : v0[e];
             if (EPI == EPI_RESID) {
-              const float h = p.resid[o] + v;
-              p.resid[o] = h;
-              if (p.hg_out) {
-                p.hg_out[o] = f32_to_bf16(h * gn);
-                ss[e] += h * h;
-              }
+              p.resid[o] += v;
             } else {
               if (p.y_f32) p.y_f32[o] = v;
               if (p.y_bf16) p.y_bf16[o] = f32_to_bf16(v);
             }
-          }
-        }
-        if (EPI == EPI_RESID && p.hg_out) {
-          // the logical tile's 32 rows are one 32-column group of the next RMSNorm
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float y = ss[e];
-            y += __shfl_xor(y, 1, 16);
-            y += __shfl_xor(y, 2, 16);
-            y += __shfl_xor(y, 4, 16);
-            y += __shfl_xor(y, 8, 16);
-            const int tok = tb * 64 + t * 16 + 4 * b + e;
-            if (j == 0 && tok < p.T) p.ssq_out[(size_t)tok * p.ssq_n + L] = y;
           }
         }
       }

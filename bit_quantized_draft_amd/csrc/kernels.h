@@ -15,6 +15,10 @@ enum Epilogue { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
 // the GEMM's lane order followed by 16 rows x 2 groups of (scale, zero) fp16 pairs.
 constexpr int TILE_BLOCK_BYTES = 1024 + 16 * 2 * 4;
 
+// Folded RMSNorm: the sums of h^2 of a token row come in groups of 256 columns (ssq[t][g],
+// g < ssq_groups(H)), written by resid_finish / row_stats.
+inline int ssq_groups(int H) { return (H + 255) / 256; }
+
 // ------------------------------------------------------------------ W4A16 GEMM (gemm_w4.hip)
 
 // Decomposition of one int4 GEMM: units = token blocks x tile groups x K ranges; a unit is
@@ -48,15 +52,10 @@ struct W4Args {
   uint16_t* u_bf16;
   bool defer_reduce;   // split K ranges: leave the partials to the consumer
   // RMSNorm folded into a consumer GEMM: x = bf16(h * gain), outputs of token row t scaled
-  // by 1 / sqrt(sum(ssq_in[t][0 .. ssq_n)) / rms_H + rms_eps)
+  // by 1 / sqrt(sum(ssq_in[t][0 .. ssq_n)) / rms_H + rms_eps); ssq_n = ssq_groups(H)
   const float* ssq_in;
   int ssq_n, rms_H;
   float rms_eps;
-  // RMSNorm inputs written by an EPI_RESID GEMM without K split: hg_out = bf16(h * hg_gain),
-  // ssq_out[t][n / 32] (ssq_n groups)
-  uint16_t* hg_out;
-  const uint16_t* hg_gain;
-  float* ssq_out;
 };
 hipError_t launch_w4(const W4Args& a, const W4Plan& pl, void* ws, hipStream_t st);
 
@@ -95,9 +94,9 @@ hipError_t gemm_bf16_wait_expired(int* expired);
 
 // ------------------------------------------------------------------ layer glue (misc.hip)
 
-// Finish a residual GEMM whose K was split: h32[t][n] += sum over splits of part[s][t][n]
-// (range order), then, with a gain, the next RMSNorm's inputs hg = bf16(h32 * gain) and
-// ssq[t][n / 32] (sums of h^2 per 32 columns). H % 32 == 0.
+// Finish a residual GEMM: with splits > 1, h32[t][n] += sum over splits of part[s][t][n]
+// (range order); then, with a gain, the next RMSNorm's inputs hg = bf16(h32 * gain) and
+// ssq[t][g] (sums of h^2 per 256-column group g). row_stats: the same without partials.
 hipError_t launch_resid_finish(const float* part, int splits, float* h32, int T, int H, const uint16_t* gain,
                                uint16_t* hg, float* ssq, hipStream_t st);
 hipError_t launch_row_stats(const float* h32, int T, int H, const uint16_t* gain, uint16_t* hg, float* ssq,

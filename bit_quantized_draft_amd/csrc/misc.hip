@@ -96,63 +96,45 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
 
 // ------------------------------------------------------------------ split-K finish
 
-// Residual GEMM whose K was split into ranges: thread (token blockIdx.y, column n) adds the
-// ranges' partials in range order (a fixed order) to h32, and with a gain writes the next
-// RMSNorm's inputs: hg = bf16(h * gain) and ssq[t][n / 32], the 32-column group's sum of
-// h^2 (the group's 32 lanes, fixed xor tree).
+// Finish of a residual GEMM: workgroup (column block blockIdx.x of 256, token blockIdx.y).
+// With K split into ranges (splits > 1) each thread adds the ranges' partials of its column
+// in range order (a fixed order) to h32; with splits <= 1 h32 is already final. With a gain
+// it then writes the next RMSNorm's inputs: hg = bf16(h * gain) and ssq[t][blockIdx.x], the
+// block's sum of h^2 (each wave's xor tree, then the four waves in order).
 __global__ __launch_bounds__(256) void resid_finish_kernel(const float* __restrict__ part, int splits, int T,
                                                            int H, float* __restrict__ h32,
                                                            const uint16_t* __restrict__ gain,
                                                            uint16_t* __restrict__ hg, float* __restrict__ ssq) {
+  __shared__ float wsum[4];
   const int tok = blockIdx.y;
-  const int n = blockIdx.x * 256 + threadIdx.x;   // H % 32 == 0: a 32-lane group is all in or all out
-  if (n >= H) return;
-  const size_t slice = (size_t)T * H;
-  const float* src = part + (size_t)tok * H + n;
-  float sum = 0.f;
-  for (int s0 = 0; s0 < splits; s0 += 8) {   // eight independent loads in flight, added in order
-    float x[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = s0 + i < splits ? src[(size_t)(s0 + i) * slice] : 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (s0 + i < splits) sum += x[i];
-  }
+  const int n = blockIdx.x * 256 + threadIdx.x;
   const size_t o = (size_t)tok * H + n;
-  const float h = h32[o] + sum;
-  h32[o] = h;
-  if (!gain) return;
-  hg[o] = f32_to_bf16(h * bf16_to_f32(gain[n]));
-  float x = h * h;
-  x += __shfl_xor(x, 1, 32);
-  x += __shfl_xor(x, 2, 32);
-  x += __shfl_xor(x, 4, 32);
-  x += __shfl_xor(x, 8, 32);
-  x += __shfl_xor(x, 16, 32);
-  if ((n & 31) == 0) ssq[(size_t)tok * (H >> 5) + (n >> 5)] = x;
-}
-
-// The first RMSNorm's inputs from h32 (one workgroup per token row): hg = bf16(h * gain)
-// and ssq[t][n / 32], each 32-column group's sum of h^2 (32 lanes, fixed order).
-__global__ __launch_bounds__(256) void row_stats_kernel(const float* __restrict__ h32, int H,
-                                                        const uint16_t* __restrict__ gain,
-                                                        uint16_t* __restrict__ hg, float* __restrict__ ssq) {
-  const int t = blockIdx.x;
-  for (int n0 = 0; n0 < H; n0 += blockDim.x) {
-    const int n = n0 + threadIdx.x;
-    float x = 0.f;
-    if (n < H) {
-      const float h = h32[(size_t)t * H + n];
-      hg[(size_t)t * H + n] = f32_to_bf16(h * bf16_to_f32(gain[n]));
-      x = h * h;
+  float h = 0.f;
+  if (n < H) {
+    h = h32[o];
+    if (splits > 1) {
+      const size_t slice = (size_t)T * H;
+      const float* src = part + o;
+      float sum = 0.f;
+      for (int s0 = 0; s0 < splits; s0 += 8) {   // eight independent loads in flight, added in order
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = s0 + i < splits ? src[(size_t)(s0 + i) * slice] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (s0 + i < splits) sum += x[i];
+      }
+      h += sum;
+      h32[o] = h;
     }
-    x += __shfl_xor(x, 1, 32);
-    x += __shfl_xor(x, 2, 32);
-    x += __shfl_xor(x, 4, 32);
-    x += __shfl_xor(x, 8, 32);
-    x += __shfl_xor(x, 16, 32);
-    if ((threadIdx.x & 31) == 0 && n < H) ssq[(size_t)t * (H >> 5) + (n >> 5)] = x;
   }
+  if (!gain) return;
+  if (n < H) hg[o] = f32_to_bf16(h * bf16_to_f32(gain[n]));
+  const float x = wave_sum(n < H ? h * h : 0.f);
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = x;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    ssq[(size_t)tok * gridDim.x + blockIdx.x] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
 }
 
 // RoPE table of a step (every layer uses the same positions): rope[t][i] = (cos, sin) of
@@ -218,18 +200,16 @@ __global__ __launch_bounds__(256) void qkv_finish_kernel(const float* __restrict
 
 hipError_t launch_resid_finish(const float* part, int splits, float* h32, int T, int H, const uint16_t* gain,
                                uint16_t* hg, float* ssq, hipStream_t st) {
-  if (splits <= 1) return hipSuccess;
-  if (!part || (H & 31) || (gain && (!hg || !ssq))) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(resid_finish_kernel, dim3((H + 255) / 256, T), dim3(256), 0, st, part, splits, T, H, h32, gain,
+  if (splits <= 1 && !gain) return hipSuccess;   // nothing to add, no norm inputs wanted
+  if ((splits > 1 && !part) || !h32 || H < 1 || (gain && (!hg || !ssq))) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(resid_finish_kernel, dim3(ssq_groups(H), T), dim3(256), 0, st, part, splits, T, H, h32, gain,
                      hg, ssq);
   return hipGetLastError();
 }
 
 hipError_t launch_row_stats(const float* h32, int T, int H, const uint16_t* gain, uint16_t* hg, float* ssq,
                             hipStream_t st) {
-  if (H & 31) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(row_stats_kernel, dim3(T), dim3(256), 0, st, h32, H, gain, hg, ssq);
-  return hipGetLastError();
+  return launch_resid_finish(nullptr, 0, const_cast<float*>(h32), T, H, gain, hg, ssq, st);
 }
 
 hipError_t launch_rope_table(const int32_t* depth, int T, int C, int hd, float theta, float2* rope,
