@@ -10,8 +10,8 @@ import ctypes
 
 import torch
 
-from ._lib import (SS_BF16, SS_W4G64, SS_W4G64_TILED, SsAttnArgs, SsLayer, SsLinear, SsModel, SsStepArgs,
-                   SubspecError, check, lib)
+from ._lib import (SS_BF16, SS_ERR_INVALID_ARG, SS_ERR_UNSUPPORTED, SS_W4G64, SS_W4G64_TILED, SsAttnArgs,
+                   SsLayer, SsLinear, SsModel, SsStepArgs, SubspecError, check, lib)
 
 
 def _stream():
@@ -22,9 +22,51 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _need(t, dtype, name):
-    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
-        raise TypeError(f"{name} must be a contiguous CUDA tensor of dtype {dtype}")
+def _on_device(t):
+    return t.is_cuda
+
+
+def _bad(msg):
+    return SubspecError(SS_ERR_INVALID_ARG, msg)
+
+
+def _need(t, dtype, name, shape=None):
+    """A contiguous device tensor of this dtype and, when given, exactly this shape (a
+    mismatch would make the library read or write outside the tensor)."""
+    dtypes = dtype if isinstance(dtype, tuple) else (dtype,)
+    if not isinstance(t, torch.Tensor) or t.dtype not in dtypes or not _on_device(t) or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous CUDA tensor of dtype {' or '.join(map(str, dtypes))}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise _bad(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _need_2d(t, dtype, name):
+    _need(t, dtype, name)
+    if t.dim() != 2:
+        raise _bad(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    return t.shape
+
+
+def _need_vec(t, dtype, name, n):
+    _need(t, dtype, name)
+    if t.numel() != n:
+        raise _bad(f"{name} must hold {n} elements, got {t.numel()}")
+
+
+def _need_w4(q, s, z, n, k, what):
+    _need(q, torch.uint8, f"{what} qweight", (n, k // 2))
+    _need(s, torch.float16, f"{what} scale", (n, k // 64))
+    _need(z, torch.float16, f"{what} zero", (n, k // 64))
+
+
+def _need_tiled(tw, n, k):
+    if not isinstance(tw, TiledW4):
+        raise TypeError("weight must be a TiledW4")
+    if (tw.n, tw.k) != (n, k):
+        raise _bad(f"tiled weight is [{tw.n}][{tw.k}], expected [{n}][{k}]")
+    _need(tw.data, torch.uint8, "tiled weight data")
+    if tw.data.numel() < lib().ss_w4_tiled_bytes(n, k):
+        raise _bad(f"tiled weight data holds {tw.data.numel()} bytes, {lib().ss_w4_tiled_bytes(n, k)} needed")
 
 
 def _workspace(nbytes, device, ws=None):
@@ -43,8 +85,7 @@ def abi_version():
 
 def quantize_substitute(w, group=64):
     """bf16 W [n][k] -> (qweight u8 [n][k/2], scale fp16 [n][k/64], zero fp16 [n][k/64])."""
-    _need(w, torch.bfloat16, "w")
-    n, k = w.shape
+    n, k = _need_2d(w, torch.bfloat16, "w")
     q = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
     s = torch.empty((n, k // 64), dtype=torch.float16, device=w.device)
     z = torch.empty((n, k // 64), dtype=torch.float16, device=w.device)
@@ -53,8 +94,8 @@ def quantize_substitute(w, group=64):
 
 
 def dequantize_substitute(q, s, z, group=64):
-    _need(q, torch.uint8, "qweight")
-    n, kh = q.shape
+    n, kh = _need_2d(q, torch.uint8, "qweight")
+    _need_w4(q, s, z, n, kh * 2, "dequantize")
     out = torch.empty((n, kh * 2), dtype=torch.float16, device=q.device)
     check(lib().ss_dequantize_substitute(_ptr(q), _ptr(s), _ptr(z), n, kh * 2, group, _ptr(out),
                                          _stream()))
@@ -71,12 +112,12 @@ class TiledW4:
 
 def w4_tile(q, s, z):
     """(qweight, scale, zero) of an int4 weight [n][k] -> TiledW4."""
-    _need(q, torch.uint8, "qweight")
-    n, kh = q.shape
+    n, kh = _need_2d(q, torch.uint8, "qweight")
     k = kh * 2
+    _need_w4(q, s, z, n, k, "w4_tile")
     nbytes = lib().ss_w4_tiled_bytes(n, k)
     if nbytes == 0:
-        raise SubspecError(f"w4_tile: unsupported shape n={n} k={k}")
+        raise SubspecError(SS_ERR_UNSUPPORTED, f"w4_tile: unsupported shape n={n} k={k}")
     t = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     check(lib().ss_w4_tile(_ptr(q), _ptr(s), _ptr(z), n, k, _ptr(t), _stream()))
     return TiledW4(t, n, k)
@@ -86,9 +127,9 @@ def w4_tile(q, s, z):
 
 def w4a16_linear(x, q, s, z, want_bf16=True, want_f32=True, workspace=None):
     """Y = X deq(W)^T; returns (y_bf16 or None, y_f32 or None)."""
-    _need(x, torch.bfloat16, "x")
-    T, k = x.shape
-    n = q.shape[0]
+    T, k = _need_2d(x, torch.bfloat16, "x")
+    n = _need_2d(q, torch.uint8, "qweight")[0]
+    _need_w4(q, s, z, n, k, "w4a16_linear")
     yb = torch.empty((T, n), dtype=torch.bfloat16, device=x.device) if want_bf16 else None
     yf = torch.empty((T, n), dtype=torch.float32, device=x.device) if want_f32 else None
     nbytes = lib().ss_w4a16_linear_workspace(T, n, k)
@@ -100,9 +141,14 @@ def w4a16_linear(x, q, s, z, want_bf16=True, want_f32=True, workspace=None):
 
 def w4a16_gate_up_swiglu(x, q, s, z, out=None, workspace=None):
     """u = silu(X Wg^T) * (X Wu^T) with the fused int4 gate_up weight [2I][k]; u bf16 [T][I]."""
-    _need(x, torch.bfloat16, "x")
-    T, k = x.shape
-    I = q.shape[0] // 2
+    T, k = _need_2d(x, torch.bfloat16, "x")
+    n2 = _need_2d(q, torch.uint8, "qweight")[0]
+    if n2 % 2:
+        raise _bad(f"gate_up weight has {n2} rows, an odd count")
+    I = n2 // 2
+    _need_w4(q, s, z, n2, k, "w4a16_gate_up_swiglu")
+    if out is not None:
+        _need(out, torch.bfloat16, "out", (T, I))
     u = torch.empty((T, I), dtype=torch.bfloat16, device=x.device) if out is None else out
     nbytes = lib().ss_w4a16_gate_up_swiglu_workspace(T, I, k)
     ws = _workspace(nbytes, x.device, workspace)
@@ -113,9 +159,9 @@ def w4a16_gate_up_swiglu(x, q, s, z, out=None, workspace=None):
 
 def w4a16_linear_tiled(x, tw, want_bf16=True, want_f32=True, workspace=None):
     """w4a16_linear on a TiledW4 weight."""
-    _need(x, torch.bfloat16, "x")
-    T, k = x.shape
+    T, k = _need_2d(x, torch.bfloat16, "x")
     n = tw.n
+    _need_tiled(tw, n, k)
     yb = torch.empty((T, n), dtype=torch.bfloat16, device=x.device) if want_bf16 else None
     yf = torch.empty((T, n), dtype=torch.float32, device=x.device) if want_f32 else None
     nbytes = lib().ss_w4a16_linear_workspace(T, n, k)
@@ -127,9 +173,13 @@ def w4a16_linear_tiled(x, tw, want_bf16=True, want_f32=True, workspace=None):
 
 def w4a16_gate_up_swiglu_tiled(x, tw, out=None, workspace=None):
     """w4a16_gate_up_swiglu on a TiledW4 weight [2I][k]."""
-    _need(x, torch.bfloat16, "x")
-    T, k = x.shape
+    T, k = _need_2d(x, torch.bfloat16, "x")
+    _need_tiled(tw, tw.n, k)
+    if tw.n % 2:
+        raise _bad(f"gate_up weight has {tw.n} rows, an odd count")
     I = tw.n // 2
+    if out is not None:
+        _need(out, torch.bfloat16, "out", (T, I))
     u = torch.empty((T, I), dtype=torch.bfloat16, device=x.device) if out is None else out
     nbytes = lib().ss_w4a16_gate_up_swiglu_workspace(T, I, k)
     ws = _workspace(nbytes, x.device, workspace)
@@ -139,10 +189,9 @@ def w4a16_gate_up_swiglu_tiled(x, tw, out=None, workspace=None):
 
 
 def bf16_linear(x, w, want_bf16=True, want_f32=True, workspace=None):
-    _need(x, torch.bfloat16, "x")
-    _need(w, torch.bfloat16, "w")
-    T, k = x.shape
-    n = w.shape[0]
+    T, k = _need_2d(x, torch.bfloat16, "x")
+    n = _need_2d(w, torch.bfloat16, "w")[0]
+    _need(w, torch.bfloat16, "w", (n, k))
     yb = torch.empty((T, n), dtype=torch.bfloat16, device=x.device) if want_bf16 else None
     yf = torch.empty((T, n), dtype=torch.float32, device=x.device) if want_f32 else None
     nbytes = lib().ss_bf16_linear_workspace(T, n, k)
@@ -165,6 +214,8 @@ def tree_validate(parents):
 def tree_mask(parents):
     """Ancestor-or-self mask (int64 view of the uint64 words) [T][ceil(T/64)] and depth [T]."""
     _need(parents, torch.int32, "parents")
+    if parents.dim() != 1:
+        raise _bad(f"parents must be 1-D, got shape {tuple(parents.shape)}")
     T = parents.numel()
     W = (T + 63) // 64
     mask = torch.empty((T, W), dtype=torch.int64, device=parents.device)
@@ -177,8 +228,20 @@ def tree_attention(q, k_cache, v_cache, k_tree, v_tree, parents, C, sm_scale=0.0
                    want_bf16=True, want_f32=False, want_mask=False, workspace=None):
     """Tree attention; q [T][nq][hd], caches [nkv][c_stride][hd], tree K/V [nkv][T][hd]."""
     _need(q, torch.bfloat16, "q")
+    if q.dim() != 3:
+        raise _bad(f"q must be [T][nq][hd], got shape {tuple(q.shape)}")
     T, nq, hd = q.shape
+    _need(k_cache, torch.bfloat16, "k_cache")
+    if k_cache.dim() != 3:
+        raise _bad(f"k_cache must be [nkv][c_stride][hd], got shape {tuple(k_cache.shape)}")
     nkv, c_stride, _ = k_cache.shape
+    _need(k_cache, torch.bfloat16, "k_cache", (nkv, c_stride, hd))
+    _need(v_cache, torch.bfloat16, "v_cache", (nkv, c_stride, hd))
+    _need(k_tree, torch.bfloat16, "k_tree", (nkv, T, hd))
+    _need(v_tree, torch.bfloat16, "v_tree", (nkv, T, hd))
+    _need_vec(parents, torch.int32, "parents", T)
+    if not 0 <= C <= c_stride:
+        raise _bad(f"C={C} outside 0..{c_stride}")
     dev = q.device
     out = torch.empty((T, nq, hd), dtype=torch.bfloat16, device=dev) if want_bf16 else None
     outf = torch.empty((T, nq, hd), dtype=torch.float32, device=dev) if want_f32 else None
@@ -199,8 +262,9 @@ def tree_attention(q, k_cache, v_cache, k_tree, v_tree, parents, C, sm_scale=0.0
 # ------------------------------------------------------------------ verification / selection
 
 def row_argmax(logits, out=None):
-    _need(logits, torch.float32, "logits")
-    R, V = logits.shape
+    R, V = _need_2d(logits, torch.float32, "logits")
+    if out is not None:
+        _need(out, torch.int32, "out", (R,))
     out = torch.empty(R, dtype=torch.int32, device=logits.device) if out is None else out
     check(lib().ss_row_argmax(_ptr(logits), R, V, _ptr(out), _stream()))
     return out
@@ -208,8 +272,15 @@ def row_argmax(logits, out=None):
 
 def tree_accept(parents, tokens, target_argmax, out=None):
     """Returns device tensors (path [T], accept_len [1], bonus [1])."""
+    _need(parents, torch.int32, "parents")
     T = parents.numel()
+    _need_vec(tokens, torch.int32, "tokens", T)
+    _need_vec(target_argmax, torch.int32, "target_argmax", T)
     dev = parents.device
+    if out is not None:
+        _need_vec(out[0], torch.int32, "path", T)
+        _need_vec(out[1], torch.int32, "accept_len", 1)
+        _need_vec(out[2], torch.int32, "bonus", 1)
     if out is None:
         path = torch.empty(T, dtype=torch.int32, device=dev)
         ln = torch.empty(1, dtype=torch.int32, device=dev)
@@ -222,8 +293,11 @@ def tree_accept(parents, tokens, target_argmax, out=None):
 
 
 def draft_select(logits, gumbel, inv_temp, k, out=None, workspace=None):
-    _need(logits, torch.float32, "logits")
-    R, V = logits.shape
+    R, V = _need_2d(logits, torch.float32, "logits")
+    if gumbel is not None:
+        _need(gumbel, torch.float32, "gumbel", (R, V))
+    if out is not None:
+        _need(out, torch.int32, "out", (R, k))
     out = torch.empty((R, k), dtype=torch.int32, device=logits.device) if out is None else out
     nbytes = lib().ss_draft_select_workspace(R, V, k)
     ws = _workspace(nbytes, logits.device, workspace)
@@ -255,10 +329,21 @@ def kv_commit(k_caches, v_caches, tree_k, tree_v, C, path, accept_len):
     """Copy the root's and the accepted path's tree K/V rows of every layer into the
     caches at rows C .. C + L (path / accept_len: device outputs of tree_accept)."""
     L = len(k_caches)
-    if not (len(v_caches) == len(tree_k) == len(tree_v) == L):
-        raise SubspecError("kv_commit: one cache and one tree K/V per layer")
+    if L < 1 or not (len(v_caches) == len(tree_k) == len(tree_v) == L):
+        raise _bad("kv_commit: one cache and one tree K/V per layer")
+    b16 = (torch.bfloat16, torch.int16, torch.uint16)   # rows are copied as 2-byte words
+    _need(k_caches[0], b16, "k_caches[0]")
+    if k_caches[0].dim() != 3 or tree_k[0].dim() != 3:
+        raise _bad("kv_commit: caches are [nkv][c_stride][hd] and tree K/V [nkv][T][hd]")
     nkv, c_stride, hd = k_caches[0].shape
     T = tree_k[0].shape[1]
+    for l in range(L):
+        _need(k_caches[l], b16, f"k_caches[{l}]", (nkv, c_stride, hd))
+        _need(v_caches[l], b16, f"v_caches[{l}]", (nkv, c_stride, hd))
+        _need(tree_k[l], b16, f"tree_k[{l}]", (nkv, T, hd))
+        _need(tree_v[l], b16, f"tree_v[{l}]", (nkv, T, hd))
+    _need_vec(path, torch.int32, "path", T)
+    _need_vec(accept_len, torch.int32, "accept_len", 1)
     arr = lambda ts: (ctypes.c_void_p * L)(*[t.data_ptr() for t in ts])
     check(lib().ss_kv_commit(arr(k_caches), arr(v_caches), arr(tree_k), arr(tree_v), L, nkv, hd, c_stride,
                              C, T, _ptr(path), _ptr(accept_len), _stream()))
@@ -299,8 +384,27 @@ class SubstituteModel:
     def draft_tree_step(self, parents, C, tree_k, tree_v, tokens=None, hidden_in=None,
                         hidden_out=None, logits=None, logit_rows=None, workspace=None):
         """One substitute-stack step over the T tree tokens (outputs written in place)."""
+        _need(parents, torch.int32, "parents")
         T = parents.numel()
         L = self.L
+        if len(tree_k) != L or len(tree_v) != L:
+            raise _bad(f"tree_k / tree_v need one tensor per layer ({L})")
+        for l in range(L):
+            _need(tree_k[l], torch.bfloat16, f"tree_k[{l}]", (self.nkv, T, self.hd))
+            _need(tree_v[l], torch.bfloat16, f"tree_v[{l}]", (self.nkv, T, self.hd))
+        if tokens is not None:
+            _need_vec(tokens, torch.int32, "tokens", T)
+        if hidden_in is not None:
+            _need(hidden_in, torch.bfloat16, "hidden_in", (T, self.H))
+        if tokens is None and hidden_in is None:
+            raise _bad("tokens or hidden_in is needed")
+        if hidden_out is not None:
+            _need(hidden_out, torch.bfloat16, "hidden_out", (T, self.H))
+        if logit_rows is not None:
+            _need(logit_rows, torch.int32, "logit_rows")
+        if logits is not None:
+            R = T if logit_rows is None else logit_rows.numel()
+            _need(logits, torch.float32, "logits", (R, self.V))
         tk = (ctypes.c_void_p * L)(*[t.data_ptr() for t in tree_k])
         tv = (ctypes.c_void_p * L)(*[t.data_ptr() for t in tree_v])
         a = SsStepArgs(tokens=None if tokens is None else tokens.data_ptr(),
@@ -321,6 +425,7 @@ class SubstituteModel:
 
 
 __all__ = ["abi_version", "quantize_substitute", "dequantize_substitute", "w4a16_linear",
-           "w4a16_gate_up_swiglu", "TiledW4", "w4_tile", "w4a16_linear_tiled", "w4a16_gate_up_swiglu_tiled",
+           "w4a16_gate_up_swiglu", "TiledW4", "w4_tile", "w4a16_linear_tiled",
+           "w4a16_gate_up_swiglu_tiled",
            "bf16_linear", "tree_validate", "tree_mask", "tree_attention", "row_argmax",
            "tree_accept", "kv_commit", "draft_select", "draft_select_workspace_bytes", "SubstituteModel", "SubspecError"]

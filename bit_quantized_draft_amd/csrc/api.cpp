@@ -63,10 +63,11 @@ ss_status check_device(const char* fn) {
     (void)hipGetLastError();
     return fail(SS_ERR_DEVICE, "%s: no HIP device available (%s)", fn, hipGetErrorString(e));
   }
+  constexpr int MAX_DEV = 64;
+  if (dev >= MAX_DEV) return fail(SS_ERR_DEVICE, "%s: device id %d beyond %d", fn, dev, MAX_DEV - 1);
   static std::mutex mu;
-  static std::vector<int> state;  // 0 unknown, 1 ok, 2 bad
+  static int state[MAX_DEV] = {};  // 0 unknown, 1 ok, 2 bad
   std::lock_guard<std::mutex> lk(mu);
-  if ((int)state.size() <= dev) state.resize(dev + 1, 0);
   if (state[dev] == 0) {
     hipDeviceProp_t prop;
     e = hipGetDeviceProperties(&prop, dev);
