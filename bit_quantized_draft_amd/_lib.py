@@ -73,6 +73,8 @@ SIGNATURES = {
     "ss_w4_tile": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_void_p]),
     "ss_w4a16_linear_tiled": (c_int, [c_void_p, c_int32, c_void_p, c_int64, c_int64, c_void_p, c_void_p,
                                       c_void_p, c_size_t, c_void_p]),
+    "ss_w4a16_linear_tiled_noalloc": (c_int, [c_void_p, c_int32, c_void_p, c_int64, c_int64, c_void_p,
+                                              c_void_p, c_void_p]),
     "ss_w4a16_gate_up_swiglu_tiled": (c_int, [c_void_p, c_int32, c_void_p, c_int64, c_int64, c_void_p,
                                               c_void_p, c_size_t, c_void_p]),
     "ss_kv_commit": (c_int, [POINTER(c_void_p), POINTER(c_void_p), POINTER(c_void_p), POINTER(c_void_p),

@@ -171,6 +171,20 @@ def w4a16_linear_tiled(x, tw, want_bf16=True, want_f32=True, workspace=None):
     return yb, yf
 
 
+def w4a16_linear_tiled_noalloc(x, tw, yb, yf):
+    """w4a16_linear_tiled into caller-provided outputs (bf16 and/or fp32 [T][n], either may be
+    None), with the library's device scratch for partial sums: no allocation anywhere."""
+    T, k = _need_2d(x, torch.bfloat16, "x")
+    n = tw.n
+    _need_tiled(tw, n, k)
+    if yb is not None:
+        _need(yb, torch.bfloat16, "yb", (T, n))
+    if yf is not None:
+        _need(yf, torch.float32, "yf", (T, n))
+    check(lib().ss_w4a16_linear_tiled_noalloc(_ptr(x), T, _ptr(tw.data), n, k, _ptr(yb), _ptr(yf), _stream()))
+    return yb, yf
+
+
 def w4a16_gate_up_swiglu_tiled(x, tw, out=None, workspace=None):
     """w4a16_gate_up_swiglu on a TiledW4 weight [2I][k]."""
     T, k = _need_2d(x, torch.bfloat16, "x")
@@ -425,7 +439,7 @@ class SubstituteModel:
 
 
 __all__ = ["abi_version", "quantize_substitute", "dequantize_substitute", "w4a16_linear",
-           "w4a16_gate_up_swiglu", "TiledW4", "w4_tile", "w4a16_linear_tiled",
+           "w4a16_gate_up_swiglu", "TiledW4", "w4_tile", "w4a16_linear_tiled", "w4a16_linear_tiled_noalloc",
            "w4a16_gate_up_swiglu_tiled",
            "bf16_linear", "tree_validate", "tree_mask", "tree_attention", "row_argmax",
            "tree_accept", "kv_commit", "draft_select", "draft_select_workspace_bytes", "SubstituteModel", "SubspecError"]

@@ -410,6 +410,30 @@ ss_status ss_w4a16_linear_tiled(const void* x_bf16, int32_t T, const void* tiled
   return w4_linear(__func__, x_bf16, T, w, n, k, y_bf16, y_f32, workspace, ws_bytes, stream);
 }
 
+ss_status ss_w4a16_linear_tiled_noalloc(const void* x_bf16, int32_t T, const void* tiled, int64_t n, int64_t k,
+                                        void* y_bf16, float* y_f32, void* stream) {
+  const char* fn = __func__;
+  ss_status s = linear_sizes(fn, T, n, k);
+  if (s != SS_OK) return s;
+  const ss::W4Plan pl = ss::plan_w4(T, (int)n, (int)k, ss::EPI_STORE, 0, true);
+  if (pl.ws_bytes > ss::W4_SCRATCH_BYTES)
+    return fail(SS_ERR_WORKSPACE, "%s: this shape needs %zu bytes of partial sums, beyond the %zu-byte device scratch",
+                fn, pl.ws_bytes, ss::W4_SCRATCH_BYTES);
+  if ((s = linear_common(fn, x_bf16, T, n, k, y_bf16, y_f32, nullptr, 0, 0)) != SS_OK) return s;
+  const ss_linear w{SS_W4G64_TILED, tiled, nullptr, nullptr, nullptr};
+  if ((s = check_linear(fn, w, "weight")) != SS_OK) return s;
+  if ((s = check_device(fn)) != SS_OK) return s;
+  void* scratch = nullptr;
+  const hipError_t e = ss::w4_scratch(&scratch);
+  if (e != hipSuccess) return fail(SS_ERR_DEVICE, "%s: device scratch address: %s", fn, hipGetErrorString(e));
+  ss::W4Args a = w4_args(x_bf16, T, w, (int)n, (int)k);
+  a.epi = ss::EPI_STORE;
+  a.y_f32 = y_f32;
+  a.y_bf16 = static_cast<uint16_t*>(y_bf16);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return launched(fn, ss::launch_w4(a, pl, scratch, st), st);
+}
+
 ss_status ss_w4a16_gate_up_swiglu_tiled(const void* x_bf16, int32_t T, const void* tiled, int64_t I, int64_t k,
                                         void* u_bf16, void* workspace, size_t ws_bytes, void* stream) {
   const ss_linear w{SS_W4G64_TILED, tiled, nullptr, nullptr, nullptr};

@@ -37,6 +37,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 namespace ss {
 
@@ -151,6 +152,31 @@ W4Plan plan_w4(int T, int N, int K, int epi, int swiglu_I, bool reduce_launch) {
   best.G = std::min(best.units, MAX_WGS);
   best.ws_bytes = best.splits > 1 ? align256((size_t)best.splits * T * best.nout * sizeof(float)) : 0;
   return best;
+}
+
+// ------------------------------------------------------------------ no-allocation scratch
+
+// Partial sums of the no-allocation entry point: one array per device, held until the
+// process ends. Host code passes its device address (scratch_ptrs), never the symbol.
+static __device__ __align__(256) unsigned char scratch[W4_SCRATCH_BYTES];
+
+hipError_t w4_scratch(void** out) {
+  constexpr int MAX_DEV = 64;
+  static std::mutex mu;
+  static void* scratch_ptrs[MAX_DEV] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEV) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!scratch_ptrs[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    scratch_ptrs[dev] = ptr;
+  }
+  *out = scratch_ptrs[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_w4(const W4Args& a, const W4Plan& pl, void* ws, hipStream_t st) {

@@ -58,6 +58,10 @@ struct W4Args {
   float rms_eps;
 };
 hipError_t launch_w4(const W4Args& a, const W4Plan& pl, void* ws, hipStream_t st);
+// Device scratch of the no-allocation linear (file-scope array in gemm_w4.hip): its bytes,
+// and its address on the current device (looked up once per device).
+constexpr size_t W4_SCRATCH_BYTES = (size_t)16 << 20;
+hipError_t w4_scratch(void** out);
 
 // ------------------------------------------------------------------ bf16-weight GEMM (gemm_bf16.hip)
 

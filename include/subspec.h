@@ -114,6 +114,18 @@ ss_status ss_w4a16_gate_up_swiglu_tiled(const void* x_bf16, int32_t T, const voi
                                         int64_t k, void* u_bf16, void* workspace, size_t ws_bytes,
                                         void* stream);
 
+/* ss_w4a16_linear_tiled without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc). The K-range partial sums go to a device array
+ * of the library (16 MiB, one per GPU, held until the process ends) instead of a caller
+ * workspace; the result is the one ss_w4a16_linear_tiled computes. Shapes whose partial
+ * sums exceed the array (ss_w4a16_linear_workspace(T, n, k) > 16 MiB) are rejected with
+ * SS_ERR_WORKSPACE. Every call on a GPU uses that GPU's one array: calls that overlap in
+ * time on one GPU (other streams, other threads) race and must be serialized by the
+ * caller. Same-stream calls are ordered and safe. */
+ss_status ss_w4a16_linear_tiled_noalloc(const void* x_bf16, int32_t T, const void* tiled, int64_t n,
+                                        int64_t k, void* y_bf16, float* y_f32, void* stream);
+
 /* Dense bf16-weight linear layer, for layers the draft shares with the target
  * unquantized ([Review] §2.2 step 4: layers that fit on the GPU stay shared with the
  * target; here the LM head) and for the target verify pass. W bf16 [n][k]; otherwise

@@ -71,6 +71,8 @@ def test_tiled_shapes():
     _bad(api.w4a16_linear_tiled, bf(T, 2 * k), tw)                       # tw.k != x's k
     short = api.TiledW4(u8(100), n, k)
     _bad(api.w4a16_linear_tiled, bf(T, k), short)                        # data too small
+    _bad(api.w4a16_linear_tiled_noalloc, bf(T, k), tw, bf(T, n + 16), None)
+    _bad(api.w4a16_linear_tiled_noalloc, bf(T, k), tw, None, f32(T + 1, n))
     _bad(api.w4a16_gate_up_swiglu_tiled, bf(T, k), tw, out=bf(T, n))    # out is [T][n/2]
 
 
