@@ -155,3 +155,37 @@ def test_step_kv_cache_may_be_null_only_without_prefix(L):
     model, args, _keep1, _keep2 = _dummy_step(C=5)
     assert L.ss_draft_tree_step(ctypes.byref(model), ctypes.byref(args), None, 0, None) == _lib.SS_ERR_INVALID_ARG
     assert b"null KV cache" in L.ss_last_error()
+
+
+def test_misaligned_pointers_are_rejected_on_the_host(L):
+    """Device pointers must meet the alignment the kernels' vector loads assume (16 bytes for
+    bf16 activations, code bytes and workspaces, 2 for bf16 outputs, 4 for fp32 outputs);
+    a misaligned one is rejected with SS_ERR_INVALID_ARG before anything is launched."""
+    ok = ctypes.c_void_p(1 << 20)
+    for bad_x in (ctypes.c_void_p((1 << 20) + 2), ctypes.c_void_p((1 << 20) + 8)):
+        assert L.ss_w4a16_linear_tiled(bad_x, 4, ok, 16, 128, ok, None, None, 0, None) == _lib.SS_ERR_INVALID_ARG
+        assert b"align" in L.ss_last_error()
+    # misaligned fp32 output
+    assert L.ss_w4a16_linear_tiled(ok, 4, ok, 16, 128, None, ctypes.c_void_p((1 << 20) + 2), None, 0, None) \
+        == _lib.SS_ERR_INVALID_ARG
+    # misaligned tiled weight
+    assert L.ss_w4a16_linear_tiled(ok, 4, ctypes.c_void_p((1 << 20) + 4), 16, 128, ok, None, None, 0, None) \
+        == _lib.SS_ERR_INVALID_ARG
+    # misaligned workspace on a shape that needs one
+    T, n, k = 64, 3584, 18944
+    need = L.ss_w4a16_linear_workspace(T, n, k)
+    assert need > 0
+    assert L.ss_w4a16_linear_tiled(ok, T, ok, n, k, ok, None, ctypes.c_void_p((1 << 20) + 8), need, None) \
+        == _lib.SS_ERR_INVALID_ARG
+
+
+@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="a GPU driver is present: the no-device path is not reachable")
+def test_no_device_is_reported_not_crashed(L):
+    """Without a HIP device every compute entry point returns SS_ERR_DEVICE with a message
+    once its arguments are valid (the pointers are never dereferenced)."""
+    ok = ctypes.c_void_p(1 << 20)
+    assert L.ss_w4a16_linear_tiled(ok, 4, ok, 16, 128, ok, None, None, 0, None) == _lib.SS_ERR_DEVICE
+    assert b"device" in L.ss_last_error()
+    assert L.ss_w4a16_linear_tiled_noalloc(ok, 4, ok, 16, 128, ok, None, None) == _lib.SS_ERR_DEVICE
+    assert L.ss_row_argmax(ctypes.cast(ok, ctypes.POINTER(ctypes.c_float)), 4, 100,
+                           ctypes.cast(ok, ctypes.POINTER(ctypes.c_int32)), None) == _lib.SS_ERR_DEVICE

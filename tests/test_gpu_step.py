@@ -126,10 +126,67 @@ def test_small_stack_with_lm_head(L, T, C, V, kind, rows, wl):
     assert_close(host(logits), ref_lg, scale_abs=True, what="logits")
 
 
-def test_step_rejects_bad_tree_under_debug_sync():
-    # validation on the host side of the binding: a non-topological parent array
+def test_tree_validate_rejects_non_topological_parents_on_the_host():
     with pytest.raises(bq.SubspecError):
         bq.tree_validate([-1, 2, 0])
+
+
+_DEBUG_SYNC_SCRIPT = r"""
+import json, sys, torch
+sys.path.insert(0, sys.argv[1])
+import bit_quantized_draft_amd as bq
+from bit_quantized_draft_amd._lib import STATUS_NAMES
+torch.manual_seed(0)
+dev = torch.device("cuda:0")
+H, I, nq, nkv, hd, V, T, cs = 128, 256, 2, 1, 64, 64, 4, 16
+r = lambda *s: (0.05 * torch.randn(*s)).to(torch.bfloat16).to(dev)
+ly = dict(qkv=r((nq + 2 * nkv) * hd, H), o=r(H, nq * hd), gate_up=r(2 * I, H), down=r(H, I),
+          norm1=r(H) + 1, norm2=r(H) + 1, k_cache=r(nkv, cs, hd), v_cache=r(nkv, cs, hd))
+m = bq.SubstituteModel(H, I, nq, nkv, hd, [ly], V=V, embed=r(V, H), final_norm=r(H) + 1, lm_head=r(V, H))
+tk = [torch.empty((nkv, T, hd), dtype=torch.bfloat16, device=dev)]
+tv = [torch.empty((nkv, T, hd), dtype=torch.bfloat16, device=dev)]
+i32 = lambda v: torch.tensor(v, dtype=torch.int32, device=dev)
+good_par, good_tok = i32([-1, 0, 0, 1]), i32([1, 2, 3, 4])
+cases = {"ok": (good_par, good_tok, None),
+         "bad_tree": (i32([-1, 2, 0, 1]), good_tok, None),
+         "bad_token": (good_par, i32([1, 2, V, 4]), None),
+         "bad_logit_row": (good_par, good_tok, i32([0, T]))}
+out = {}
+for name, (par, tok, rows) in cases.items():
+    print("case", name, flush=True)
+    R = T if rows is None else rows.numel()
+    logits = torch.empty((R, V), dtype=torch.float32, device=dev)
+    try:
+        m.draft_tree_step(par, 8, tk, tv, tokens=tok, logits=logits, logit_rows=rows)
+        torch.cuda.synchronize()
+        out[name] = "SS_OK"
+    except bq.SubspecError as e:
+        out[name] = STATUS_NAMES.get(e.status, str(e.status)) + " " + str(e)
+print("RESULT " + json.dumps(out), flush=True)
+"""
+
+
+def test_step_error_word_under_debug_sync():
+    """With SS_DEBUG_SYNC=1 (set in a fresh process before any GPU call) the step reports
+    the device-side checks: a non-topological parent array (SS_ERR_BAD_TREE), a token id
+    outside [0, V) and a logit row outside [0, T) (SS_ERR_INVALID_ARG). The kernels that
+    detect them are bounds-safe on such input (the mask walk is bounded, the embedding and
+    the final norm write zeros for the bad rows), so nothing faults."""
+    import json
+    import os
+    import subprocess
+    import sys
+    env = dict(os.environ, SS_DEBUG_SYNC="1")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    p = subprocess.run([sys.executable, "-c", _DEBUG_SYNC_SCRIPT, root], env=env, capture_output=True, text=True,
+                       timeout=240)
+    print(p.stdout[-2000:], p.stderr[-2000:], flush=True)
+    assert p.returncode == 0
+    res = json.loads([l for l in p.stdout.splitlines() if l.startswith("RESULT ")][-1][7:])
+    assert res["ok"] == "SS_OK"
+    assert res["bad_tree"].startswith("SS_ERR_BAD_TREE")
+    assert res["bad_token"].startswith("SS_ERR_INVALID_ARG") and "token id" in res["bad_token"]
+    assert res["bad_logit_row"].startswith("SS_ERR_INVALID_ARG") and "logit row" in res["bad_logit_row"]
 
 
 def test_tiled_step_is_bit_identical_to_plain():
