@@ -2,8 +2,11 @@
 
 Every substitute linear shape of the three model families (Qwen2.5-7B, Qwen2.5-32B and
 Llama-3.1-8B shaped layers) runs through the C ABI at the tree size its workload uses
-(T = 64 / 48 for the 7B and 8B shapes, T = 256 for the 32B shapes), in the launch
-configuration the bench uses. Weights and activations come from the seeded generators;
+(T = 64 / 48 for the 7B and 8B shapes, T = 256 for the 32B shapes), on the plain int4
+layout (compared with the oracle on sampled rows) and on the tiled layout the bench
+streams (compared bit for bit with the plain layout's output: the same arithmetic on
+relocated codes). The bf16 LM heads of the 7B and 8B families (V = 152064 and 128256) are
+compared with the oracle on sampled vocabulary rows. Weights and activations come from the seeded generators;
 the GPU quantizes the whole bf16 matrix, the oracle quantizes only the sampled rows
 (quantization is per row and group, so the rows are independent), and both the codes
 and the outputs of those rows are compared. Attention at the 32B workload's size
@@ -71,6 +74,10 @@ def test_w4a16_linear_fullsize_sampled(name, N, K, T):
     q_o, s_o, z_o = _check_rows_quant(q[ridx], s[ridx], z[ridx], w[rows])
     ref = oracle.w4a16_matmul64(x, q_o, s_o, z_o)
     assert_close(host(yf)[:, rows], ref, what=f"{name} fp32 (sampled rows)")
+    # the tiled layout the bench streams: bit-identical to the plain layout's output
+    _, yt = bq.w4a16_linear_tiled(to_bf16(x), bq.w4_tile(q, s, z), want_bf16=False)
+    torch.cuda.synchronize()
+    assert torch.equal(yt, yf), f"{name}: tiled output differs from the plain layout's"
 
 
 @pytest.mark.parametrize("name,I,K,T", GATE_UP)
@@ -91,6 +98,25 @@ def test_gate_up_swiglu_fullsize_sampled(name, I, K, T):
     ref = oracle.swiglu64(y[:, :n], y[:, n:])
     got = oracle.bf16_to_f64(bf16_bits(u))[:, g_rows]
     assert_close(got, ref, scale_abs=True, bf16_out=True, what=f"{name} u (sampled rows)")
+    ut = bq.w4a16_gate_up_swiglu_tiled(to_bf16(x), bq.w4_tile(q, s, z))
+    torch.cuda.synchronize()
+    assert torch.equal(ut.view(torch.int16), u.view(torch.int16)), f"{name}: tiled u differs from the plain layout's"
+
+
+@pytest.mark.parametrize("name,V,H,T", [("7b.lm_head", 152064, 3584, 64), ("8b.lm_head", 128256, 4096, 48)])
+def test_lm_head_fullsize_sampled(name, V, H, T):
+    """The dense bf16 LM head at the full vocabulary (the draft step's last GEMM and the
+    verify pass's), against the oracle's fp64 product on sampled vocabulary rows."""
+    print(f"full-size LM head {name}: V={V} H={H} T={T}", flush=True)
+    seed = V + H
+    w = gen.normal_bf16((V, H), 0.05, seed, 13, gen.TID_LMHEAD)
+    x = gen.normal_bf16((T, H), 1.0, seed, 13, gen.TID_X)
+    yb, yf = bq.bf16_linear(to_bf16(x), to_bf16(w))
+    torch.cuda.synchronize()
+    rows = _rows(V, seed, n=256)
+    ref = oracle.matmul64(oracle.bf16_to_f64(x), oracle.bf16_to_f64(w[rows]))
+    assert_close(host(yf)[:, rows], ref, scale_abs=True, what=f"{name} logits (sampled rows)")
+    assert np.array_equal(bf16_bits(yb)[:, rows], oracle.f32_to_bf16(host(yf)[:, rows]))
 
 
 def test_tree_attention_32b_workload_one_kv_head():

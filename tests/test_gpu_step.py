@@ -74,6 +74,10 @@ def small_cfg(**kw):
     (dict(nq=4, nkv=4, hd=64, H=256, I=512), 1, 0, "R", "tiled"),       # root only, no prefix
     (dict(nq=4, nkv=2, hd=64, H=256, I=512), 256, 64, "RB", "tiled"),   # largest tree: 4 token blocks
     (dict(H=3584, I=18944, nq=28, nkv=4, hd=128, cid=2), 64, 2048, "CB", "bf16"),   # target verify layer
+    # Llama-3.1-8B-shaped long-context layer (theta 5e5, eps 1e-5), the workload's tree and prefix
+    (dict(H=4096, I=14336, nq=32, nkv=8, hd=128, cid=5, rope_theta=5e5, eps=1e-5), 48, 16384, "CB", "tiled"),
+    # Qwen2.5-32B-shaped layer at the 256-token random-branching tree, C = 4096
+    (dict(H=5120, I=27648, nq=40, nkv=8, hd=128, cid=4), 256, 4096, "RB", "tiled"),
 ])
 def test_one_layer_parity(cfgkw, T, C, kind, wl):
     cfg = small_cfg(**cfgkw)
