@@ -49,6 +49,12 @@ def parse():
     ap.add_argument("--mfma-probe", action="store_true",
                     help="MFMA utilisation at the large-tree workload: the four tiled int4 linears "
                          "of a Qwen2.5-32B-shaped layer at T=256, timed against the dense bf16 peak")
+    ap.add_argument("--extra-steps", type=int, default=10,
+                    help="timed step replays of the Qwen2.5-32B and Llama-3.1-8B shaped stacks")
+    ap.add_argument("--no-extra", action="store_true", help="skip the 32B and 8B stack steps")
+    ap.add_argument("--extra-only", type=int, choices=(4, 5), default=None,
+                    help="run only the step of workload 4 (Qwen2.5-32B stack) or 5 (Llama-3.1-8B "
+                         "long-context stack) and print its entry (for kernel traces)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) of "
                          "--pmc-probe into the traffic summary under profiles/ (CPU only)")
@@ -108,6 +114,136 @@ def algorithmic_bytes_step(cfg, n_layers):
     per_layer += 2 * cfg.nkv * T * cfg.hd * 2                        # tree K/V written
     head = cfg.V * cfg.H * 2 + T * cfg.V * 4 + T * cfg.H * 2
     return n_layers * per_layer + head
+
+
+# ------------------------------------------------------------------ the 32B and 8B stacks
+
+MFMA_PEAK_TFLOPS = 2500.0   # dense bf16
+
+
+def step_flops(cfg, n_layers):
+    """Multiply-add flops of one draft step: the four linears over all T tree tokens, the
+    tree attention (scores and values over C + T keys) and the LM head."""
+    from synth.configs import layer_shapes
+    T, C = cfg.T, cfg.C
+    lin = sum(N * K for _, N, K in layer_shapes(cfg))
+    per_layer = 2.0 * T * lin + 4.0 * T * (C + T) * cfg.nq * cfg.hd
+    return n_layers * per_layer + (2.0 * T * cfg.V * cfg.H if cfg.V else 0.0)
+
+
+def extra_config(cid, args, dev):
+    """One draft step of workload cid (4: 64-layer Qwen2.5-32B-shaped stack, T = 256, C =
+    4096; 5: 32-layer Llama-3.1-8B-shaped stack, T = 48, C = 16384, bf16 LM head and child
+    selection at temperatures 0.2 and 0.6), captured in a HIP graph, checked against its
+    eager run and timed over args.extra_steps replays with HIP events."""
+    import torch
+    import bit_quantized_draft_amd as bq
+    from synth import gen
+    from synth.configs import get_config, layer_shapes
+    cfg = get_config(cid)
+    L, T, C, V = cfg.L, cfg.T, cfg.C, cfg.V
+    log(f"building {cfg.name}: {L} layers, T={T}, C={C}")
+    ones = torch.ones(cfg.H, dtype=torch.bfloat16, device=dev)
+    layers = []
+    for li in range(L):
+        d = {}
+        for name, N, K in layer_shapes(cfg):
+            w = gen.torch_normal_bf16((N, K), cfg.w_std, 0, cfg.cid, gen.TID_W, li * 16 + gen.SLOT[name], dev)
+            d[name] = bq.w4_tile(*bq.quantize_substitute(w))
+            del w
+        kc = gen.torch_normal_bf16((cfg.nkv, C, cfg.hd), 1.0, 0, cfg.cid, gen.TID_KC, li, dev)
+        vc = gen.torch_normal_bf16((cfg.nkv, C, cfg.hd), 1.0, 0, cfg.cid, gen.TID_VC, li, dev)
+        d.update(norm1=ones, norm2=ones, k_cache=kc, v_cache=vc)
+        layers.append(d)
+        if li % 16 == 0:
+            log(f"  layer {li} built")
+    kw = dict(rope_theta=cfg.rope_theta, rms_eps=cfg.eps)
+    if V:
+        kw.update(V=V, embed=gen.torch_normal_bf16((V, cfg.H), cfg.w_std, 0, cfg.cid, gen.TID_EMBED, 0, dev),
+                  final_norm=ones,
+                  lm_head=gen.torch_normal_bf16((V, cfg.H), cfg.w_std, 0, cfg.cid, gen.TID_LMHEAD, 0, dev))
+    model = bq.SubstituteModel(cfg.H, cfg.I, cfg.nq, cfg.nkv, cfg.hd, layers, **kw)
+    par_np = gen.tree_parents(T, cfg.tree, cfg.depth_cap, seed=0, cid=cfg.cid)
+    par = torch.from_numpy(par_np).to(dev)
+    # with a vocabulary the step starts from token ids (embedding gather); without one (the
+    # 32B workload names no head) it starts from seeded hidden states
+    tok = torch.from_numpy(gen.tree_tokens(par_np, V, seed=0, cid=cfg.cid)).to(dev) if V else None
+    h_in = None if V else gen.torch_normal_bf16((T, cfg.H), 1.0, 0, cfg.cid, gen.TID_HIDDEN, 0, dev)
+    tk = [torch.empty((cfg.nkv, T, cfg.hd), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    tv = [torch.empty((cfg.nkv, T, cfg.hd), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    hout = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev)
+    logits = torch.empty((T, V), dtype=torch.float32, device=dev) if V else None
+    ws = torch.empty(model.workspace_bytes(T, C), dtype=torch.uint8, device=dev)
+    temps = cfg.temps if V else ()
+    kids = {t: torch.empty((T, TOPK), dtype=torch.int32, device=dev) for t in temps}
+    ws_s = torch.empty(max(1, bq.draft_select_workspace_bytes(T, V, TOPK)) if V else 1, dtype=torch.uint8,
+                       device=dev)
+    inv = {t: float(np.float32(1.0) / np.float32(t)) for t in temps}
+
+    def step():
+        model.draft_tree_step(par, C, tk, tv, tokens=tok, hidden_in=h_in, hidden_out=hout, logits=logits,
+                              workspace=ws)
+
+    def select(t):
+        bq.draft_select(logits, None, inv[t], TOPK, out=kids[t], workspace=ws_s)
+
+    step()
+    for t in temps:
+        select(t)
+    torch.cuda.synchronize()
+    ref_h = hout.clone()
+    ref_k = {t: kids[t].clone() for t in temps}
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g_step = torch.cuda.CUDAGraph()
+    g_sel = {t: torch.cuda.CUDAGraph() for t in temps}
+    with torch.cuda.stream(stream):
+        step()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g_step, stream=stream):
+            step()
+        for t in temps:
+            with torch.cuda.graph(g_sel[t], stream=stream):
+                select(t)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        g_step.replay()
+        for t in temps:
+            g_sel[t].replay()
+        torch.cuda.synchronize()
+        assert torch.equal(hout, ref_h), f"{cfg.name}: graph replay differs from the eager step"
+        for t in temps:
+            assert torch.equal(kids[t], ref_k[t]), f"{cfg.name}: selection replay differs at t={t}"
+        step()
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g_step.replay()   # steady state
+    e0.record()
+    for _ in range(args.extra_steps):
+        g_step.replay()
+    e1.record(); torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.extra_steps
+    ms_sel = {}
+    for t in temps:
+        e0.record()
+        for _ in range(args.extra_steps):
+            g_sel[t].replay()
+        e1.record(); torch.cuda.synchronize()
+        ms_sel[t] = e0.elapsed_time(e1) / args.extra_steps
+    alg = algorithmic_bytes_step(cfg, L)
+    flops = step_flops(cfg, L)
+    entry = {"workload": f"{cfg.name}: {L}-layer substitute stack, T={T} tree tokens ({cfg.tree} tree), C={C}"
+                         + (f", bf16 LM head (vocab {V}) + child selection" if V else ""),
+             "step_ms": round(ms_step, 4), "tree_tokens_per_s": round(T / (ms_step * 1e-3), 1),
+             "alg_bytes": int(alg), "hbm_frac": round(alg / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+             "mfma_flops": int(flops), "mfma_frac": round(flops / (ms_step * 1e-3) / (MFMA_PEAK_TFLOPS * 1e12), 4),
+             "steps_timed": args.extra_steps}
+    for t in temps:
+        entry[f"select_t{t}_ms"] = round(ms_sel[t], 4)
+        entry[f"tree_tokens_per_s_t{t}"] = round(T / ((ms_step + ms_sel[t]) * 1e-3), 1)
+    del layers, model, ws
+    torch.cuda.empty_cache()
+    return entry
 
 
 # ------------------------------------------------------------------ CPU oracle baseline
@@ -363,6 +499,12 @@ def main():
     if args.mfma_probe:
         mfma_probe(args)
         return
+    if args.extra_only:
+        import torch
+        dev = torch.device("cuda:0")
+        torch.cuda.set_device(dev)
+        print(json.dumps({f"workload_{args.extra_only}": extra_config(args.extra_only, args, dev)}), flush=True)
+        return
     import torch
     import bit_quantized_draft_amd as bq
     from synth import gen
@@ -513,6 +655,14 @@ def main():
     gu_bytes = gate_up_bytes(cfg)
     achieved = gu_bytes / (us_launch * 1e-6) / 1e9
 
+    # the other single-GPU workloads: the 32B stack at T = 256 and the 8B long-context stack
+    extra = {}
+    if not args.no_extra:
+        del draft, target, ws_d, ws_t, g_draft, g_verify
+        torch.cuda.empty_cache()
+        for cid in (4, 5):
+            extra[f"workload_{cid}"] = extra_config(cid, args, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, n_layers)
@@ -529,7 +679,8 @@ def main():
                    "tree_tokens_per_cycle": DRAFT_STEPS * T, "accept_len": L,
                    "draft_step_ms": round(ms_draft_step, 4), "verify_ms": round(ms_verify, 4),
                    "draft_step_alg_bytes": int(step_bytes),
-                   "draft_step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4)},
+                   "draft_step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                   "other_workloads": extra},
         "roofline": {"kernel": "w4k_kernel<TT=4, EPI_SWIGLU, tiled> (tiled int4 gate_up 37888x3584, T=64)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
