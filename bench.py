@@ -118,9 +118,6 @@ def algorithmic_bytes_step(cfg, n_layers):
 
 # ------------------------------------------------------------------ the 32B and 8B stacks
 
-MFMA_PEAK_TFLOPS = 2500.0   # dense bf16
-
-
 def step_flops(cfg, n_layers):
     """Multiply-add flops of one draft step: the four linears over all T tree tokens, the
     tree attention (scores and values over C + T keys) and the LM head."""
