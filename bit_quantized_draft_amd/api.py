@@ -320,6 +320,42 @@ def draft_select(logits, gumbel, inv_temp, k, out=None, workspace=None):
     return out
 
 
+class TreeState:
+    """Device state of the draft-tree expansion: parents / tokens int32 [T] (the draft
+    step's inputs), cum fp32 [T], frontier int32 [R] (the next step's logit rows) and meta
+    int32 [4] = {nodes, frontier size, step, 0}."""
+
+    def __init__(self, T, D, R, k, device):
+        self.T, self.D, self.R, self.k = T, D, R, k
+        self.parents = torch.empty(T, dtype=torch.int32, device=device)
+        self.tokens = torch.empty(T, dtype=torch.int32, device=device)
+        self.cum = torch.empty(T, dtype=torch.float32, device=device)
+        self.frontier = torch.empty(R, dtype=torch.int32, device=device)
+        self.meta = torch.empty(4, dtype=torch.int32, device=device)
+        self._ws = None
+
+    def _args(self):
+        return (_ptr(self.parents), _ptr(self.tokens), _ptr(self.cum), _ptr(self.frontier), _ptr(self.meta))
+
+
+def tree_expand_init(state, root_token):
+    """The template before step 0: the root alone."""
+    check(lib().ss_tree_expand_init(int(root_token), state.T, state.D, state.R, state.k, *state._args(), _stream()))
+
+
+def tree_expand(state, logits, children, inv_temp, workspace=None):
+    """One expansion step from the frontier rows' logits [R][V] and their children [R][k]."""
+    R, V = _need_2d(logits, torch.float32, "logits")
+    if R != state.R:
+        raise _bad(f"logits has {R} rows, the state's frontier {state.R}")
+    _need(children, torch.int32, "children", (state.R, state.k))
+    nbytes = lib().ss_tree_expand_workspace(state.R, V)
+    ws = _workspace(nbytes, logits.device, workspace if workspace is not None else state._ws)
+    state._ws = ws
+    check(lib().ss_tree_expand(_ptr(logits), _ptr(children), state.R, V, float(inv_temp), state.k, state.T, state.D,
+                               *state._args(), _ptr(ws), nbytes, _stream()))
+
+
 def draft_select_workspace_bytes(rows, vocab, k):
     """Workspace bytes ss_draft_select needs for this shape (0: none)."""
     return lib().ss_draft_select_workspace(rows, vocab, k)
@@ -442,4 +478,5 @@ __all__ = ["abi_version", "quantize_substitute", "dequantize_substitute", "w4a16
            "w4a16_gate_up_swiglu", "TiledW4", "w4_tile", "w4a16_linear_tiled", "w4a16_linear_tiled_noalloc",
            "w4a16_gate_up_swiglu_tiled",
            "bf16_linear", "tree_validate", "tree_mask", "tree_attention", "row_argmax",
-           "tree_accept", "kv_commit", "draft_select", "draft_select_workspace_bytes", "SubstituteModel", "SubspecError"]
+           "tree_accept", "kv_commit", "draft_select", "draft_select_workspace_bytes", "TreeState",
+           "tree_expand_init", "tree_expand", "SubstituteModel", "SubspecError"]

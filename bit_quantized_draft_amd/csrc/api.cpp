@@ -761,6 +761,52 @@ ss_status ss_tree_accept(const int32_t* parents, const int32_t* tokens, const in
   return debug_validate_parents(fn, parents, T, st);
 }
 
+static ss_status expand_sizes(const char* fn, int32_t R, int32_t k, int32_t T, int32_t D) {
+  if (T < 2 || T > 256) return fail(SS_ERR_UNSUPPORTED, "%s: T must be in 2..256 (got %d)", fn, T);
+  if (D < 1 || D > T - 1) return fail(SS_ERR_INVALID_ARG, "%s: D must be in 1..T-1 (got %d)", fn, D);
+  if (R < (T - 1 + D - 1) / D) return fail(SS_ERR_INVALID_ARG, "%s: R = %d rows cannot hold the %d nodes a step adds",
+                                           fn, R, (T - 1 + D - 1) / D);
+  if (k < R || k * R > 64) return fail(SS_ERR_UNSUPPORTED, "%s: need R <= k and k * R <= 64 (k=%d, R=%d)", fn, k, R);
+  return SS_OK;
+}
+
+ss_status ss_tree_expand_init(int32_t root_token, int32_t T, int32_t D, int32_t R, int32_t k, int32_t* parents,
+                              int32_t* tokens, float* cum, int32_t* frontier, int32_t* meta, void* stream) {
+  const char* fn = __func__;
+  ss_status s = expand_sizes(fn, R, k, T, D);
+  if (s != SS_OK) return s;
+  if (root_token < 0) return fail(SS_ERR_INVALID_ARG, "%s: root_token must be a token id", fn);
+  REQ_PTR(parents, 4); REQ_PTR(tokens, 4); REQ_PTR(cum, 4); REQ_PTR(frontier, 4); REQ_PTR(meta, 4);
+  if ((s = check_device(fn)) != SS_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return launched(fn, ss::launch_expand_init(root_token, T, R, parents, tokens, cum, frontier, meta, st), st);
+}
+
+size_t ss_tree_expand_workspace(int32_t R, int32_t V) {
+  if (R < 1 || R > 64 || V < 1) return 0;
+  return ss::expand_ws_bytes(R, V);
+}
+
+ss_status ss_tree_expand(const float* logits, const int32_t* children, int32_t R, int32_t V, float inv_temp,
+                         int32_t k, int32_t T, int32_t D, int32_t* parents, int32_t* tokens, float* cum,
+                         int32_t* frontier, int32_t* meta, void* workspace, size_t ws_bytes, void* stream) {
+  const char* fn = __func__;
+  ss_status s = expand_sizes(fn, R, k, T, D);
+  if (s != SS_OK) return s;
+  if (V < k) return fail(SS_ERR_INVALID_ARG, "%s: vocab %d smaller than k %d", fn, V, k);
+  if (!(inv_temp > 0.f) || !std::isfinite(inv_temp)) return fail(SS_ERR_INVALID_ARG, "%s: inv_temp must be > 0", fn);
+  REQ_PTR(logits, 4); REQ_PTR(children, 4);
+  REQ_PTR(parents, 4); REQ_PTR(tokens, 4); REQ_PTR(cum, 4); REQ_PTR(frontier, 4); REQ_PTR(meta, 4);
+  const size_t need = ss::expand_ws_bytes(R, V);
+  if (!workspace || ws_bytes < need)
+    return fail(SS_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace ? ws_bytes : 0);
+  REQ_PTR(workspace, 16);
+  if ((s = check_device(fn)) != SS_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return launched(fn, ss::launch_expand(logits, children, R, V, inv_temp, k, T, D, parents, tokens, cum, frontier,
+                                        meta, workspace, st), st);
+}
+
 ss_status ss_kv_commit(void* const* k_cache, void* const* v_cache, const void* const* k_tree,
                        const void* const* v_tree, int32_t layers, int32_t nkv, int32_t hd, int32_t c_stride,
                        int32_t C, int32_t T, const int32_t* path, const int32_t* accept_len, void* stream) {

@@ -175,6 +175,14 @@ hipError_t launch_draft_select(const float* logits, const float* gumbel, int row
                                float inv_temp, int k, int32_t* out, void* ws, hipStream_t st);
 // workspace bytes of launch_draft_select (0: one pass, no workspace)
 size_t draft_select_ws_bytes(int rows, int vocab, int k);
+// draft-tree expansion (ss_tree_expand): lse partials of the frontier rows, then one wave
+// that scores, picks and appends; meta = {nodes, frontier size, step, 0}
+size_t expand_ws_bytes(int R, int vocab);
+hipError_t launch_expand_init(int root_token, int T, int R, int32_t* parents, int32_t* tokens, float* cum,
+                              int32_t* frontier, int32_t* meta, hipStream_t st);
+hipError_t launch_expand(const float* logits, const int32_t* children, int R, int vocab, float inv_temp, int k,
+                         int T, int D, int32_t* parents, int32_t* tokens, float* cum, int32_t* frontier,
+                         int32_t* meta, void* ws, hipStream_t st);
 hipError_t launch_tree_accept(const int32_t* parents, const int32_t* tokens, const int32_t* tgt,
                               int T, int32_t* path, int32_t* len, int32_t* bonus, hipStream_t st);
 

@@ -526,6 +526,160 @@ size_t draft_select_ws_bytes(int rows, int vocab, int k) {
   return ((n * sizeof(float) + 255) & ~(size_t)255) + n * sizeof(int32_t);
 }
 
+// ------------------------------------------------------------------ draft-tree expansion
+
+// Log-sum-exp partials of the frontier rows' sharpened logits y = fp32(l * inv_temp):
+// workgroup (part blockIdx.x, row blockIdx.y) writes the (max, sum of exp(y - max)) of its
+// range, each thread's elements in order, then the threads in a fixed tree. Rows at or past
+// the frontier size (meta[1]) are skipped.
+__global__ __launch_bounds__(256) void expand_lse_part_kernel(const float* __restrict__ logits, int vocab,
+                                                              float inv_temp, int seg,
+                                                              const int32_t* __restrict__ meta,
+                                                              float2* __restrict__ part) {
+  __shared__ float sm[256], ss[256];
+  const int row = blockIdx.y, p = blockIdx.x;
+  if (row >= meta[1]) return;
+  const int lo = p * seg, hi = min(vocab, lo + seg);
+  const float* x = logits + (size_t)row * vocab;
+  float m = -INFINITY, sum = 0.f;
+  for (int i = lo + threadIdx.x; i < hi; i += 256) {
+    const float y = x[i] * inv_temp;
+    if (y > m) {
+      sum = sum * expf(m - y) + 1.f;
+      m = y;
+    } else {
+      sum += expf(y - m);
+    }
+  }
+  sm[threadIdx.x] = m;
+  ss[threadIdx.x] = sum;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) {
+      const float m0 = sm[threadIdx.x], m1 = sm[threadIdx.x + w];
+      const float M = fmaxf(m0, m1);
+      const float a = m0 == -INFINITY ? 0.f : ss[threadIdx.x] * expf(m0 - M);
+      const float b = m1 == -INFINITY ? 0.f : ss[threadIdx.x + w] * expf(m1 - M);
+      sm[threadIdx.x] = M;
+      ss[threadIdx.x] = a + b;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) part[(size_t)row * gridDim.x + p] = float2{sm[0], ss[0]};
+}
+
+// One expansion step (one wave): the frontier's children (ss_draft_select's top-k of the
+// same rows) scored cum[parent] + (y - lse), the B best appended at slots n .. n + B - 1
+// (ties: lower frontier position, then lower child rank), which become the frontier.
+// meta = {nodes n, frontier size, step}; a step at or past D changes nothing.
+__global__ __launch_bounds__(64) void expand_select_kernel(const float* __restrict__ logits,
+                                                           const int32_t* __restrict__ children, int R,
+                                                           int vocab, float inv_temp, int k, int T, int D,
+                                                           int parts, const float2* __restrict__ part,
+                                                           int32_t* __restrict__ parents, int32_t* __restrict__ tokens,
+                                                           float* __restrict__ cum, int32_t* __restrict__ frontier,
+                                                           int32_t* __restrict__ meta) {
+  const int lane = threadIdx.x;
+  const int n = meta[0], nf = min(meta[1], R), s = meta[2];
+  if (s >= D || n >= T) return;
+  const int B = min((T - n + (D - s) - 1) / (D - s), R);
+  // candidate lane = r * k + rank (r < nf, rank < k); k * R <= 64 (host check)
+  const int r = lane / k, rank = lane - r * k;
+  const bool live = r < nf;
+  float score = -INFINITY;
+  int token = 0, par = 0;
+  if (live) {
+    float M = -INFINITY;
+    for (int q = 0; q < parts; ++q) M = fmaxf(M, part[(size_t)r * parts + q].x);
+    float S = 0.f;
+    for (int q = 0; q < parts; ++q) {
+      const float2 v = part[(size_t)r * parts + q];
+      S += v.x == -INFINITY ? 0.f : v.y * expf(v.x - M);
+    }
+    const float lse = M + logf(S);
+    token = children[(size_t)r * k + rank];
+    par = frontier[r];
+    const float y = logits[(size_t)r * vocab + token] * inv_temp;
+    score = cum[par] + (y - lse);
+  }
+  // B rounds of a wave-wide best (score desc, then lower candidate index)
+  int chosen = -1;   // the output slot offset this lane's candidate takes
+  float cs = live ? score : -INFINITY;
+  int ci = live ? lane : 0x7FFFFFFF;
+  for (int b = 0; b < B; ++b) {
+    float bv = cs;
+    int bi = ci;
+#pragma unroll
+    for (int sh = 32; sh > 0; sh >>= 1) {
+      const float ov = __shfl_xor(bv, sh, 64);
+      const int oi = __shfl_xor(bi, sh, 64);
+      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    }
+    if (bi == lane && live && chosen < 0) {
+      chosen = b;
+      cs = -INFINITY;
+      ci = 0x7FFFFFFF;
+    }
+  }
+  __syncthreads();   // every lane has read frontier[] before it is rewritten
+  if (chosen >= 0) {
+    const int slot = n + chosen;
+    parents[slot] = par;
+    tokens[slot] = token;
+    cum[slot] = score;
+  }
+  if (lane < R) frontier[lane] = n + (lane < B ? lane : 0);
+  if (lane == 0) {
+    meta[0] = n + B;
+    meta[1] = B;
+    meta[2] = s + 1;
+  }
+}
+
+// The template before step 0: the root alone (cum 0, frontier {0}); other slots hold
+// parent 0 and the root's token (valid inputs that no real node attends to).
+__global__ __launch_bounds__(256) void expand_init_kernel(int root_token, int T, int R, int32_t* __restrict__ parents,
+                                                          int32_t* __restrict__ tokens, float* __restrict__ cum,
+                                                          int32_t* __restrict__ frontier, int32_t* __restrict__ meta) {
+  for (int i = threadIdx.x; i < T; i += blockDim.x) {
+    parents[i] = i == 0 ? -1 : 0;
+    tokens[i] = root_token;
+    cum[i] = 0.f;
+  }
+  for (int i = threadIdx.x; i < R; i += blockDim.x) frontier[i] = 0;
+  if (threadIdx.x == 0) {
+    meta[0] = 1;
+    meta[1] = 1;
+    meta[2] = 0;
+    meta[3] = 0;
+  }
+}
+
+int expand_parts(int vocab) { return std::max(1, std::min(64, vocab / 2048)); }
+
+size_t expand_ws_bytes(int R, int vocab) { return (size_t)R * expand_parts(vocab) * sizeof(float2); }
+
+hipError_t launch_expand_init(int root_token, int T, int R, int32_t* parents, int32_t* tokens, float* cum,
+                              int32_t* frontier, int32_t* meta, hipStream_t st) {
+  hipLaunchKernelGGL(expand_init_kernel, dim3(1), dim3(256), 0, st, root_token, T, R, parents, tokens, cum,
+                     frontier, meta);
+  return hipGetLastError();
+}
+
+hipError_t launch_expand(const float* logits, const int32_t* children, int R, int vocab, float inv_temp, int k,
+                         int T, int D, int32_t* parents, int32_t* tokens, float* cum, int32_t* frontier,
+                         int32_t* meta, void* ws, hipStream_t st) {
+  if (k * R > 64 || R < 1 || k < 1) return hipErrorInvalidValue;
+  const int parts = expand_parts(vocab);
+  const int seg = (vocab + parts - 1) / parts;
+  float2* part = static_cast<float2*>(ws);
+  hipLaunchKernelGGL(expand_lse_part_kernel, dim3(parts, R), dim3(256), 0, st, logits, vocab, inv_temp, seg, meta,
+                     part);
+  hipLaunchKernelGGL(expand_select_kernel, dim3(1), dim3(64), 0, st, logits, children, R, vocab, inv_temp, k, T, D,
+                     parts, part, parents, tokens, cum, frontier, meta);
+  return hipGetLastError();
+}
+
 hipError_t launch_row_argmax(const float* logits, int rows, int vocab, int32_t* out, hipStream_t st) {
   hipLaunchKernelGGL(row_argmax_kernel, dim3(rows), dim3(SCAN_THREADS), 0, st, logits, vocab, out);
   return hipGetLastError();

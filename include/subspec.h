@@ -114,6 +114,36 @@ ss_status ss_w4a16_gate_up_swiglu_tiled(const void* x_bf16, int32_t T, const voi
                                         int64_t k, void* u_bf16, void* workspace, size_t ws_bytes,
                                         void* stream);
 
+/* ------------------------------------------------------------------------------
+ * Draft-tree expansion ([Review] §6.3-§6.4: a static tree, k = 6 children per expanded
+ * node, depth 48 (§3.7); [Summary] "Approach": draft probabilities sharpened at
+ * temperature 0.2). Reading (the pages give no expansion rule): the T slots of the tree
+ * are filled over D draft steps, one level per step. Step s takes the frontier (the
+ * nodes the previous step added; the root before step 0), scores each frontier node's
+ * k children (ss_draft_select's top-k of y = fp32(l * inv_temp) with no noise) by the
+ * path's sharpened log-probability cum[parent] + y[c] - logsumexp(y), and appends the
+ * B_s = ceil((T - n) / (D - s)) best (ties: lower frontier position, then lower child
+ * rank) at slots n, n + 1, ... (n = nodes so far). They become the frontier.
+ *
+ * State (device, caller-owned, updated in place): parents int32 [T] and tokens int32 [T]
+ * (the draft step's inputs), cum fp32 [T] (path scores), frontier int32 [R] (the next
+ * step's logit rows: the frontier, padded with a valid slot), meta int32 [4] = {nodes,
+ * frontier size, step, 0}. ss_tree_expand_init sets the root (slot 0, token root_token,
+ * parent -1, score 0) and fills the other slots with parent 0 and the root's token.
+ * ss_tree_expand consumes logits fp32 [R][V] of the rows frontier[0..R) (as the draft
+ * step writes them with logit_rows = frontier, n_logit_rows = R) and children int32
+ * [R][k] (ss_draft_select on those logits, gumbel NULL, the same inv_temp); a call at
+ * step >= D changes nothing, so a captured graph may replay it freely.
+ * Requires 2 <= T <= 256, 1 <= D <= T - 1, R >= ceil((T - 1) / D), R <= k, k R <= 64.
+ * Scores are fp32 (the log-sum-exp in a fixed order); workspace: ss_tree_expand_workspace.
+ * ------------------------------------------------------------------------------ */
+ss_status ss_tree_expand_init(int32_t root_token, int32_t T, int32_t D, int32_t R, int32_t k, int32_t* parents,
+                              int32_t* tokens, float* cum, int32_t* frontier, int32_t* meta, void* stream);
+size_t ss_tree_expand_workspace(int32_t R, int32_t V);
+ss_status ss_tree_expand(const float* logits, const int32_t* children, int32_t R, int32_t V, float inv_temp,
+                         int32_t k, int32_t T, int32_t D, int32_t* parents, int32_t* tokens, float* cum,
+                         int32_t* frontier, int32_t* meta, void* workspace, size_t ws_bytes, void* stream);
+
 /* ss_w4a16_linear_tiled without a workspace argument and without any allocation, for
  * callers that cannot allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc). The K-range partial sums go to a device array
