@@ -33,6 +33,7 @@ DRAFT_STEPS = 48
 TOPK = 6
 DRAFT_TEMP = 0.2
 L_STAR = 27
+ROOT_TOKEN = 1234
 
 
 def parse():
@@ -101,9 +102,10 @@ def build_model(cfg, dev, n_layers):
     return draft, target
 
 
-def algorithmic_bytes_step(cfg, n_layers):
+def algorithmic_bytes_step(cfg, n_layers, logit_rows=None):
     """Bytes one draft step must move: int4 weights + fp16 scale/zero, prefix KV once per
-    layer, activations at kernel boundaries, bf16 LM head and fp32 logits."""
+    layer, activations at kernel boundaries, bf16 LM head and the fp32 logits of the rows
+    that need them (all T, or the expansion frontier's logit_rows)."""
     from synth.configs import layer_shapes
     T, C = cfg.T, cfg.C
     w_params = sum(N * K for _, N, K in layer_shapes(cfg))
@@ -112,7 +114,8 @@ def algorithmic_bytes_step(cfg, n_layers):
     qkvN = (cfg.nq + 2 * cfg.nkv) * cfg.hd
     per_layer += T * (cfg.H * 2 * 2 + qkvN * 2 * 2 + cfg.nq * cfg.hd * 2 * 2 + cfg.I * 2 * 2)
     per_layer += 2 * cfg.nkv * T * cfg.hd * 2                        # tree K/V written
-    head = cfg.V * cfg.H * 2 + T * cfg.V * 4 + T * cfg.H * 2
+    rows = T if logit_rows is None else logit_rows
+    head = cfg.V * cfg.H * 2 + rows * cfg.V * 4 + rows * cfg.H * 2
     return n_layers * per_layer + head
 
 
@@ -514,28 +517,35 @@ def main():
     log(f"building {cfg.name}: {n_layers} layers, T={T}, C={C}")
     draft, target = build_model(cfg, dev, n_layers)
 
-    par_np = gen.tree_parents(T, cfg.tree, cfg.depth_cap, seed=0, cid=cfg.cid)
-    tok_np = gen.tree_tokens(par_np, V, seed=0, cid=cfg.cid)
-    lg_np = gen.target_logits(par_np, tok_np, V, L_STAR, seed=0, cid=cfg.cid)
-    parents = torch.from_numpy(par_np).to(dev)
-    tokens = torch.from_numpy(tok_np).to(dev)
-    seeded_logits = torch.from_numpy(lg_np).to(dev)
+    # the draft tree is grown on the device: each draft step runs the stack over the T slots
+    # (static shape), takes the LM head on the frontier rows only, selects their k children
+    # and appends the step's quota of best children (ss_tree_expand); 48 steps fill the
+    # k=6 / depth-48 template
+    R = -(-(T - 1) // DRAFT_STEPS)
+    state = bq.TreeState(T, DRAFT_STEPS, R, TOPK, dev)
     mk = lambda: [torch.empty((cfg.nkv, T, cfg.hd), dtype=torch.bfloat16, device=dev) for _ in range(n_layers)]
     tk_d, tv_d, tk_t, tv_t = mk(), mk(), mk(), mk()
-    logits = torch.empty((T, V), dtype=torch.float32, device=dev)
+    logits = torch.empty((R, V), dtype=torch.float32, device=dev)
     vlogits = torch.empty((T, V), dtype=torch.float32, device=dev)
-    children = torch.empty((T, TOPK), dtype=torch.int32, device=dev)
+    children = torch.empty((R, TOPK), dtype=torch.int32, device=dev)
+    seeded_logits = torch.empty((T, V), dtype=torch.float32, device=dev)
     tgt = torch.empty(T, dtype=torch.int32, device=dev)
     acc_out = (torch.empty(T, dtype=torch.int32, device=dev), torch.empty(1, dtype=torch.int32, device=dev),
                torch.empty(1, dtype=torch.int32, device=dev))
     inv_t = float(np.float32(1.0) / np.float32(DRAFT_TEMP))
     ws_d = torch.empty(draft.workspace_bytes(T, C), dtype=torch.uint8, device=dev)
     ws_t = torch.empty(target.workspace_bytes(T, C), dtype=torch.uint8, device=dev)
-    ws_s = torch.empty(max(1, bq.draft_select_workspace_bytes(T, V, TOPK)), dtype=torch.uint8, device=dev)
+    ws_s = torch.empty(max(1, bq.draft_select_workspace_bytes(R, V, TOPK)), dtype=torch.uint8, device=dev)
+    parents, tokens = state.parents, state.tokens
+
+    def tree_init():
+        bq.tree_expand_init(state, ROOT_TOKEN)
 
     def draft_step():
-        draft.draft_tree_step(parents, C, tk_d, tv_d, tokens=tokens, logits=logits, workspace=ws_d)
+        draft.draft_tree_step(parents, C, tk_d, tv_d, tokens=tokens, logits=logits, logit_rows=state.frontier,
+                              workspace=ws_d)
         bq.draft_select(logits, None, inv_t, TOPK, out=children, workspace=ws_s)
+        bq.tree_expand(state, logits, children, inv_t)
 
     kc_all = [ly["k_cache"] for ly in target.layers]
     vc_all = [ly["v_cache"] for ly in target.layers]
@@ -548,39 +558,59 @@ def main():
         # cycle would advance C by L + 1; the timed cycles keep C fixed and read rows < C)
         bq.kv_commit(kc_all, vc_all, tk_t, tv_t, C, acc_out[0], acc_out[1])
 
-    # eager reference results, then capture both phases in HIP graphs
-    draft_step(); verify()
+    # eager cycle: grow the tree, then seed the target's argmax on the finished tree so the
+    # acceptance walk accepts L_STAR nodes (the draft and target weights are random); the
+    # tree is the same every cycle (the draft reads cache rows < C only)
+    tree_init()
+    for _ in range(DRAFT_STEPS):
+        draft_step()
     torch.cuda.synchronize()
-    ref_children = children.clone()
-    ref_logits_row = logits[T - 1].clone()
+    par_np, tok_np = parents.cpu().numpy(), tokens.cpu().numpy()
+    depth = np.zeros(T, dtype=np.int64)
+    assert par_np[0] == -1 and all(0 <= par_np[i] < i for i in range(1, T)), "expanded tree is not topological"
+    for i in range(1, T):
+        depth[i] = depth[par_np[i]] + 1
+    assert depth.max() == DRAFT_STEPS, f"expanded tree depth {depth.max()}, expected {DRAFT_STEPS}"
+    seeded_logits.copy_(torch.from_numpy(gen.target_logits(par_np, tok_np, V, L_STAR, seed=0, cid=cfg.cid,
+                                                           path=gen.deepest_path(par_np))))
+    verify()
+    torch.cuda.synchronize()
     ref_len = int(acc_out[1].item())
+    assert ref_len == L_STAR, f"acceptance walk returned {ref_len}, expected {L_STAR}"
+    ref_par, ref_tok, ref_cum = parents.clone(), tokens.clone(), state.cum.clone()
+
+    # capture the three phases in HIP graphs
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
-    g_draft, g_verify = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    g_init, g_draft, g_verify = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
     with torch.cuda.stream(stream):
-        draft_step(); verify()          # warm the capture stream
+        tree_init(); draft_step(); verify()          # warm the capture stream
         torch.cuda.synchronize()
+        with torch.cuda.graph(g_init, stream=stream):
+            tree_init()
         with torch.cuda.graph(g_draft, stream=stream):
             draft_step()
         with torch.cuda.graph(g_verify, stream=stream):
             verify()
     torch.cuda.synchronize()
-    # every replay checked against the eager result, with eager work in between
-    for _ in range(2):
-        g_draft.replay(); g_verify.replay()
-        torch.cuda.synchronize()
-        assert torch.equal(children, ref_children), "graph replay differs from eager run (children)"
-        assert torch.equal(logits[T - 1], ref_logits_row), "graph replay differs from eager run (logits)"
-        assert int(acc_out[1].item()) == ref_len
-        draft_step()
-        torch.cuda.synchronize()
-    assert ref_len == L_STAR, f"acceptance walk returned {ref_len}, expected {L_STAR}"
 
     def cycle():
+        g_init.replay()
         for _ in range(DRAFT_STEPS):
             g_draft.replay()
         g_verify.replay()
         return int(acc_out[1].item())      # the one host read-back per cycle
+
+    # every replayed cycle checked against the eager one, with eager work in between
+    for _ in range(2):
+        assert cycle() == L_STAR
+        assert torch.equal(parents, ref_par) and torch.equal(tokens, ref_tok), "graph cycle grew another tree"
+        assert torch.equal(state.cum, ref_cum), "graph cycle's path scores differ from the eager cycle's"
+        tree_init()
+        for _ in range(DRAFT_STEPS):
+            draft_step()
+        torch.cuda.synchronize()
+        assert torch.equal(parents, ref_par) and torch.equal(tokens, ref_tok)
 
     log(f"warmup {args.warmup} cycles")
     for _ in range(args.warmup):
@@ -598,6 +628,7 @@ def main():
 
     # phase split (outside the timed region): draft step alone and the verify phase alone
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g_init.replay()
     e0.record()
     for _ in range(DRAFT_STEPS):
         g_draft.replay()
@@ -605,7 +636,7 @@ def main():
     ms_draft_step = e0.elapsed_time(e1) / DRAFT_STEPS
     e0.record(); g_verify.replay(); e1.record(); torch.cuda.synchronize()
     ms_verify = e0.elapsed_time(e1)
-    step_bytes = algorithmic_bytes_step(cfg, n_layers)
+    step_bytes = algorithmic_bytes_step(cfg, n_layers, logit_rows=R)
     step_gbs = step_bytes / (ms_draft_step * 1e-3) / 1e9
 
     # dominant kernel: fused int4 gate_up + SwiGLU, 8 layers' weights in rotation (> 256 MB
@@ -671,8 +702,10 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16+int4",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {n_layers}-layer substitute stack, T={T} tree tokens "
-                               f"(chain+branches, depth 48), C={C}, vocab {V}; cycle = {DRAFT_STEPS} "
-                               f"draft steps + bf16 verify pass + argmax + greedy accept + KV commit",
+                               f"grown on the device to depth {DRAFT_STEPS} (k={TOPK}, {R} nodes per level at most), "
+                               f"C={C}, vocab {V}; cycle = {DRAFT_STEPS} draft steps (stack over all T slots, LM "
+                               f"head on the frontier rows, child selection at t={DRAFT_TEMP}, tree expansion) + bf16 "
+                               f"verify pass + argmax + greedy accept + KV commit",
                    "tree_tokens_per_cycle": DRAFT_STEPS * T, "accept_len": L,
                    "draft_step_ms": round(ms_draft_step, 4), "verify_ms": round(ms_verify, 4),
                    "draft_step_alg_bytes": int(step_bytes),

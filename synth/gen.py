@@ -147,17 +147,32 @@ def chain_path(parents: np.ndarray) -> list:
         path.append(cur)
 
 
-def target_logits(parents, tokens, V, L_star, seed=0, cid=0, layer=0) -> np.ndarray:
-    """Seeded target logits [T][V] fp32 with a planted acceptance of L_star chain nodes.
+def deepest_path(parents: np.ndarray) -> list:
+    """Nodes from the root to the deepest node (the lowest-index one among equals)."""
+    T = len(parents)
+    depth = np.zeros(T, dtype=np.int64)
+    for i in range(1, T):
+        depth[i] = depth[parents[i]] + 1
+    cur = int(np.argmax(depth))
+    path = [cur]
+    while cur != 0:
+        cur = int(parents[cur])
+        path.append(cur)
+    return path[::-1]
 
-    Rows are N(0,1). Along the main chain c0=0, c1, ..., the row of c_m gets
-    tokens[c_{m+1}] raised to (row max + 1) for m < L_star; the row of c_{L_star}
-    gets a token that no child of c_{L_star} carries raised the same way.
+
+def target_logits(parents, tokens, V, L_star, seed=0, cid=0, layer=0, path=None) -> np.ndarray:
+    """Seeded target logits [T][V] fp32 with a planted acceptance of L_star nodes.
+
+    Rows are N(0,1). Along the path c0=0, c1, ... (the main chain of lowest-index children
+    unless a path is given), the row of c_m gets tokens[c_{m+1}] raised to (row max + 1)
+    for m < L_star; the row of c_{L_star} gets a token that no child of c_{L_star} carries
+    raised the same way.
     """
     g = rng(seed, cid, TID_LOGIT, layer)
     T = len(parents)
     lg = g.standard_normal(size=(T, V), dtype=np.float32)
-    path = chain_path(parents)
+    path = chain_path(parents) if path is None else list(path)
     L_star = min(L_star, len(path) - 1)
     for m in range(L_star):
         row = lg[path[m]]
