@@ -73,6 +73,10 @@ SIGNATURES = {
     "ss_w4_tile": (c_int, [c_void_p, c_void_p, c_void_p, c_int64, c_int64, c_void_p, c_void_p]),
     "ss_w4a16_linear_tiled": (c_int, [c_void_p, c_int32, c_void_p, c_int64, c_int64, c_void_p, c_void_p,
                                       c_void_p, c_size_t, c_void_p]),
+    "ss_tree_accept_stochastic_workspace": (c_size_t, [c_int32, c_int32]),
+    "ss_tree_accept_stochastic": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_float,
+                                          c_float, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                          c_size_t, c_void_p]),
     "ss_tree_expand_init": (c_int, [c_int32, c_int32, c_int32, c_int32, c_int32, c_void_p, c_void_p, c_void_p,
                                     c_void_p, c_void_p, c_void_p]),
     "ss_tree_expand_workspace": (c_size_t, [c_int32, c_int32]),

@@ -320,6 +320,35 @@ def draft_select(logits, gumbel, inv_temp, k, out=None, workspace=None):
     return out
 
 
+def tree_accept_stochastic(parents, tokens, draft_logits, target_logits, inv_t_draft, inv_t_target, uniforms,
+                           bonus_uniforms, out=None, workspace=None):
+    """Multi-round speculative sampling over the tree; returns device tensors (path [T],
+    accept_len [1], bonus [1]) as tree_accept."""
+    _need(parents, torch.int32, "parents")
+    T = parents.numel()
+    _need_vec(tokens, torch.int32, "tokens", T)
+    V = _need_2d(draft_logits, torch.float32, "draft_logits")[1]
+    _need(draft_logits, torch.float32, "draft_logits", (T, V))
+    _need(target_logits, torch.float32, "target_logits", (T, V))
+    _need_vec(uniforms, torch.float64, "uniforms", T)
+    _need_vec(bonus_uniforms, torch.float64, "bonus_uniforms", T)
+    dev = parents.device
+    if out is None:
+        out = (torch.empty(T, dtype=torch.int32, device=dev), torch.empty(1, dtype=torch.int32, device=dev),
+               torch.empty(1, dtype=torch.int32, device=dev))
+    else:
+        _need_vec(out[0], torch.int32, "path", T)
+        _need_vec(out[1], torch.int32, "accept_len", 1)
+        _need_vec(out[2], torch.int32, "bonus", 1)
+    nbytes = lib().ss_tree_accept_stochastic_workspace(T, V)
+    ws = _workspace(nbytes, dev, workspace)
+    check(lib().ss_tree_accept_stochastic(_ptr(parents), _ptr(tokens), _ptr(draft_logits), _ptr(target_logits), T, V,
+                                          float(inv_t_draft), float(inv_t_target), _ptr(uniforms),
+                                          _ptr(bonus_uniforms), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), _ptr(ws),
+                                          nbytes, _stream()))
+    return out
+
+
 class TreeState:
     """Device state of the draft-tree expansion: parents / tokens int32 [T] (the draft
     step's inputs), cum fp32 [T], frontier int32 [R] (the next step's logit rows) and meta
@@ -479,4 +508,4 @@ __all__ = ["abi_version", "quantize_substitute", "dequantize_substitute", "w4a16
            "w4a16_gate_up_swiglu_tiled",
            "bf16_linear", "tree_validate", "tree_mask", "tree_attention", "row_argmax",
            "tree_accept", "kv_commit", "draft_select", "draft_select_workspace_bytes", "TreeState",
-           "tree_expand_init", "tree_expand", "SubstituteModel", "SubspecError"]
+           "tree_expand_init", "tree_expand", "tree_accept_stochastic", "SubstituteModel", "SubspecError"]

@@ -807,6 +807,38 @@ ss_status ss_tree_expand(const float* logits, const int32_t* children, int32_t R
                                         meta, workspace, st), st);
 }
 
+size_t ss_tree_accept_stochastic_workspace(int32_t T, int32_t V) {
+  if (T < 1 || T > 256 || V < 1) return 0;
+  return ss::sv_ws_bytes(T, V);
+}
+
+ss_status ss_tree_accept_stochastic(const int32_t* parents, const int32_t* tokens, const float* draft_logits,
+                                    const float* target_logits, int32_t T, int32_t V, float inv_t_draft,
+                                    float inv_t_target, const double* uniforms, const double* bonus_uniforms,
+                                    int32_t* path_out, int32_t* accept_len_out, int32_t* bonus_out, void* workspace,
+                                    size_t ws_bytes, void* stream) {
+  const char* fn = __func__;
+  if (T < 1 || T > 256) return fail(SS_ERR_UNSUPPORTED, "%s: T must be in 1..256 (got %d)", fn, T);
+  if (V < 1) return fail(SS_ERR_INVALID_ARG, "%s: V must be positive", fn);
+  if (!(inv_t_draft > 0.f) || !(inv_t_target > 0.f) || !std::isfinite(inv_t_draft) || !std::isfinite(inv_t_target))
+    return fail(SS_ERR_INVALID_ARG, "%s: the inverse temperatures must be finite and > 0", fn);
+  REQ_PTR(parents, 4); REQ_PTR(tokens, 4); REQ_PTR(draft_logits, 4); REQ_PTR(target_logits, 4);
+  REQ_PTR(uniforms, 8); REQ_PTR(bonus_uniforms, 8);
+  REQ_PTR(path_out, 4); REQ_PTR(accept_len_out, 4); REQ_PTR(bonus_out, 4);
+  const size_t need = ss::sv_ws_bytes(T, V);
+  if (!workspace || ws_bytes < need)
+    return fail(SS_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace ? ws_bytes : 0);
+  REQ_PTR(workspace, 16);
+  ss_status s = check_device(fn);
+  if (s != SS_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  s = launched(fn, ss::launch_stochastic_accept(parents, tokens, draft_logits, target_logits, T, V, inv_t_draft,
+                                                inv_t_target, uniforms, bonus_uniforms, path_out, accept_len_out,
+                                                bonus_out, workspace, st), st);
+  if (s != SS_OK) return s;
+  return debug_validate_parents(fn, parents, T, st);
+}
+
 ss_status ss_kv_commit(void* const* k_cache, void* const* v_cache, const void* const* k_tree,
                        const void* const* v_tree, int32_t layers, int32_t nkv, int32_t hd, int32_t c_stride,
                        int32_t C, int32_t T, const int32_t* path, const int32_t* accept_len, void* stream) {

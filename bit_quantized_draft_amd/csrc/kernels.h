@@ -183,6 +183,13 @@ hipError_t launch_expand_init(int root_token, int T, int R, int32_t* parents, in
 hipError_t launch_expand(const float* logits, const int32_t* children, int R, int vocab, float inv_temp, int k,
                          int T, int D, int32_t* parents, int32_t* tokens, float* cum, int32_t* frontier,
                          int32_t* meta, void* ws, hipStream_t st);
+// stochastic tree verification (ss_tree_accept_stochastic): row statistics of the target's
+// and the draft's logits, then one workgroup's multi-round speculative-sampling walk
+size_t sv_ws_bytes(int T, int V);
+hipError_t launch_stochastic_accept(const int32_t* parents, const int32_t* tokens, const float* draft_logits,
+                                    const float* target_logits, int T, int V, float inv_td, float inv_tt,
+                                    const double* uni, const double* buni, int32_t* path, int32_t* len,
+                                    int32_t* bonus, void* ws, hipStream_t st);
 hipError_t launch_tree_accept(const int32_t* parents, const int32_t* tokens, const int32_t* tgt,
                               int T, int32_t* path, int32_t* len, int32_t* bonus, hipStream_t st);
 

@@ -751,6 +751,237 @@ __global__ __launch_bounds__(64) void tree_accept_kernel(const int32_t* __restri
   }
 }
 
+// ------------------------------------------------------------------ stochastic verification
+
+// Rows 0 .. T-1: the target's logits at temperature 1/inv_tt; rows T .. 2T-1: the draft's at
+// 1/inv_td; y = fp32(l * inv). Part maxima of each row.
+__global__ __launch_bounds__(256) void sv_max_kernel(const float* __restrict__ tl, const float* __restrict__ dl,
+                                                     int T, int V, float inv_tt, float inv_td, int seg,
+                                                     float* __restrict__ pmax) {
+  __shared__ float red[256];
+  const int row = blockIdx.y, p = blockIdx.x;
+  const bool tgt = row < T;
+  const float* x = (tgt ? tl : dl) + (size_t)(tgt ? row : row - T) * V;
+  const float inv = tgt ? inv_tt : inv_td;
+  const int lo = p * seg, hi = min(V, lo + seg);
+  float m = -INFINITY;
+  for (int i = lo + threadIdx.x; i < hi; i += 256) m = fmaxf(m, x[i] * inv);
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) pmax[(size_t)row * gridDim.x + p] = red[0];
+}
+
+// Part sums of e = fp64(expf(fp32(y - M))), M the row maximum (the parts' maxima combined);
+// each thread's elements in order, then a fixed tree.
+__global__ __launch_bounds__(256) void sv_sum_kernel(const float* __restrict__ tl, const float* __restrict__ dl,
+                                                     int T, int V, float inv_tt, float inv_td, int seg,
+                                                     const float* __restrict__ pmax, double* __restrict__ psum) {
+  __shared__ double red[256];
+  const int row = blockIdx.y, p = blockIdx.x, parts = gridDim.x;
+  const bool tgt = row < T;
+  const float* x = (tgt ? tl : dl) + (size_t)(tgt ? row : row - T) * V;
+  const float inv = tgt ? inv_tt : inv_td;
+  float M = -INFINITY;
+  for (int q = 0; q < parts; ++q) M = fmaxf(M, pmax[(size_t)row * parts + q]);
+  const int lo = p * seg, hi = min(V, lo + seg);
+  double sum = 0.0;
+  for (int i = lo + threadIdx.x; i < hi; i += 256) sum += (double)expf(x[i] * inv - M);
+  red[threadIdx.x] = sum;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) psum[(size_t)row * parts + p] = red[0];
+}
+
+constexpr int SV_THREADS = 1024;
+constexpr int SV_MAX_REJ = 256;   // rejections one walk can record (at most T - 1 children)
+
+// The walk (one workgroup). At node u the current residual distribution is evaluated
+// pointwise: p = e_t / Z_t, then for each recorded rejection r: p = max(p - q, 0) / Zr[r],
+// q = e_d / Z_d. A rejection appends the V-wide sum of the new residual (fixed order);
+// a zero sum restarts from the node's own distribution.
+struct SvRow {
+  float Mt, Md;
+  double Zt, Zd;
+};
+
+__device__ __forceinline__ double sv_p(const float* tl_row, const float* dl_row, int v, float inv_tt, float inv_td,
+                                       const SvRow& r, const double* zr, int nrej) {
+  double p = (double)expf(tl_row[v] * inv_tt - r.Mt) / r.Zt;
+  if (nrej) {
+    const double q = (double)expf(dl_row[v] * inv_td - r.Md) / r.Zd;
+    for (int k = 0; k < nrej; ++k) p = fmax(p - q, 0.0) / zr[k];
+  }
+  return p;
+}
+
+__device__ double sv_block_sum(double v, double* red) {
+  red[threadIdx.x] = v;
+  __syncthreads();
+  for (int w = SV_THREADS / 2; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  const double s = red[0];
+  __syncthreads();
+  return s;
+}
+
+__global__ __launch_bounds__(SV_THREADS) void sv_walk_kernel(const int32_t* __restrict__ parents,
+                                                             const int32_t* __restrict__ tokens,
+                                                             const float* __restrict__ tl, const float* __restrict__ dl,
+                                                             int T, int V, float inv_tt, float inv_td, int parts,
+                                                             const float* __restrict__ pmax,
+                                                             const double* __restrict__ psum,
+                                                             const double* __restrict__ uni,
+                                                             const double* __restrict__ buni,
+                                                             int32_t* __restrict__ path, int32_t* __restrict__ len,
+                                                             int32_t* __restrict__ bonus) {
+  __shared__ int par[256];
+  __shared__ double red[SV_THREADS];
+  __shared__ double zr[SV_MAX_REJ];
+  __shared__ SvRow row;
+  __shared__ double s_total;
+  __shared__ int s_x[SV_THREADS / 64];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < T; i += SV_THREADS) {
+    par[i] = parents[i];
+    path[i] = -1;
+  }
+  __syncthreads();
+  int cur = 0, L = 0, nrej = 0;
+  SvRow r;
+  while (true) {
+    if (tid == 0) {
+      SvRow w;
+      w.Mt = w.Md = -INFINITY;
+      for (int q = 0; q < parts; ++q) {
+        w.Mt = fmaxf(w.Mt, pmax[(size_t)cur * parts + q]);
+        w.Md = fmaxf(w.Md, pmax[(size_t)(T + cur) * parts + q]);
+      }
+      w.Zt = w.Zd = 0.0;
+      for (int q = 0; q < parts; ++q) {
+        w.Zt += psum[(size_t)cur * parts + q];
+        w.Zd += psum[(size_t)(T + cur) * parts + q];
+      }
+      row = w;
+    }
+    __syncthreads();
+    r = row;
+    __syncthreads();
+    const float* trow = tl + (size_t)cur * V;
+    const float* drow = dl + (size_t)cur * V;
+    nrej = 0;
+    int next = -1;
+    for (int c = cur + 1; c < T; ++c) {   // children in index order (a block-uniform loop)
+      if (par[c] != cur) continue;
+      // a token id outside [0, V) is never accepted (and never read)
+      const int x = tokens[c];
+      const bool okx = x >= 0 && x < V;
+      const int xs = okx ? x : 0;
+      const double px = okx ? sv_p(trow, drow, xs, inv_tt, inv_td, r, zr, nrej) : 0.0;
+      const double qx = (double)expf(drow[xs] * inv_td - r.Md) / r.Zd;
+      if (uni[c] * qx < px) {
+        next = c;
+        break;
+      }
+      // rejected: the next residual's normalizer, the sum of max(P - Q, 0) over V
+      double part = 0.0;
+      for (int v = tid; v < V; v += SV_THREADS) {
+        const double pv = sv_p(trow, drow, v, inv_tt, inv_td, r, zr, nrej);
+        const double qv = (double)expf(drow[v] * inv_td - r.Md) / r.Zd;
+        part += fmax(pv - qv, 0.0);
+      }
+      const double z = sv_block_sum(part, red);
+      if (z > 0.0 && nrej < SV_MAX_REJ) {
+        if (tid == 0) zr[nrej] = z;
+        __syncthreads();
+        ++nrej;
+      } else {
+        nrej = 0;   // no mass left: the node's own distribution again
+      }
+    }
+    if (next < 0) break;
+    if (tid == 0) path[L] = next;
+    ++L;
+    cur = next;
+  }
+  // bonus from the residual the stopping node ended with: the lowest v whose cumulative
+  // probability exceeds u * total (thread-contiguous chunks in index order, chunk totals
+  // combined in thread order)
+  const float* trow = tl + (size_t)cur * V;
+  const float* drow = dl + (size_t)cur * V;
+  const int chunk = (V + SV_THREADS - 1) / SV_THREADS;
+  const int lo = min(V, tid * chunk), hi = min(V, lo + chunk);
+  double own = 0.0;
+  for (int v = lo; v < hi; ++v) own += sv_p(trow, drow, v, inv_tt, inv_td, r, zr, nrej);
+  red[tid] = own;
+  __syncthreads();
+  if (tid == 0) {
+    double acc = 0.0;
+    for (int t = 0; t < SV_THREADS; ++t) {
+      const double v = red[t];
+      red[t] = acc;
+      acc += v;
+    }
+    s_total = acc;
+  }
+  __syncthreads();
+  const double thr = buni[cur] * s_total;
+  int x = 0x7FFFFFFF;
+  double cum = red[tid];
+  for (int v = lo; v < hi; ++v) {
+    cum += sv_p(trow, drow, v, inv_tt, inv_td, r, zr, nrej);
+    if (cum > thr) {
+      x = v;
+      break;
+    }
+  }
+  // block minimum of the crossing points (x increases with the thread index)
+  for (int sh = 32; sh > 0; sh >>= 1) x = min(x, __shfl_xor(x, sh, 64));
+  if ((tid & 63) == 0) s_x[tid >> 6] = x;
+  __syncthreads();
+  if (tid == 0) {
+    int b = 0x7FFFFFFF;
+    for (int w = 0; w < SV_THREADS / 64; ++w) b = min(b, s_x[w]);
+    *len = L;
+    *bonus = b == 0x7FFFFFFF ? V - 1 : b;
+  }
+}
+
+int sv_parts(int V) { return std::max(1, std::min(32, V / 4096)); }
+
+size_t sv_ws_bytes(int T, int V) {
+  const size_t n = (size_t)2 * T * sv_parts(V);
+  return ((n * sizeof(float) + 255) & ~(size_t)255) + n * sizeof(double);
+}
+
+hipError_t launch_stochastic_accept(const int32_t* parents, const int32_t* tokens, const float* draft_logits,
+                                    const float* target_logits, int T, int V, float inv_td, float inv_tt,
+                                    const double* uni, const double* buni, int32_t* path, int32_t* len,
+                                    int32_t* bonus, void* ws, hipStream_t st) {
+  if (T < 1 || T > 256 || V < 1) return hipErrorInvalidValue;
+  const int parts = sv_parts(V);
+  const int seg = (V + parts - 1) / parts;
+  const size_t n = (size_t)2 * T * parts;
+  float* pmax = static_cast<float*>(ws);
+  double* psum = reinterpret_cast<double*>(static_cast<char*>(ws) + ((n * sizeof(float) + 255) & ~(size_t)255));
+  const dim3 grid(parts, 2 * T);
+  hipLaunchKernelGGL(sv_max_kernel, grid, dim3(256), 0, st, target_logits, draft_logits, T, V, inv_tt, inv_td, seg,
+                     pmax);
+  hipLaunchKernelGGL(sv_sum_kernel, grid, dim3(256), 0, st, target_logits, draft_logits, T, V, inv_tt, inv_td, seg,
+                     pmax, psum);
+  hipLaunchKernelGGL(sv_walk_kernel, dim3(1), dim3(SV_THREADS), 0, st, parents, tokens, target_logits, draft_logits, T,
+                     V, inv_tt, inv_td, parts, pmax, psum, uni, buni, path, len, bonus);
+  return hipGetLastError();
+}
+
 hipError_t launch_tree_accept(const int32_t* parents, const int32_t* tokens, const int32_t* tgt,
                               int T, int32_t* path, int32_t* len, int32_t* bonus, hipStream_t st) {
   hipLaunchKernelGGL(tree_accept_kernel, dim3(1), dim3(64), 0, st, parents, tokens, tgt, T, path, len, bonus);

@@ -114,6 +114,27 @@ ss_status ss_w4a16_gate_up_swiglu_tiled(const void* x_bf16, int32_t T, const voi
                                         int64_t k, void* u_bf16, void* workspace, size_t ws_bytes,
                                         void* stream);
 
+/* Stochastic tree verification ([Review] §3.6: target sampling at temperature 0.6 keeps
+ * the output distribution exact by speculative sampling with correction, §6.2; §6.3: the
+ * whole tree verified in one target pass). Reading (multi-round speculative sampling over
+ * the tree): P_u and Q_u are the target's and the draft's distributions at node u,
+ * softmax of y = fp32(l * inv_t) with e = fp32 exp of fp32(y - max y) widened to fp64,
+ * everything after in fp64. From the root, node u's children are tried in index order:
+ * child c (token x) is accepted iff uniforms[c] * Q_u(x) < P(x), P the current residual
+ * (P_u at first), and the walk moves to c; a rejection replaces P by max(P - Q_u, 0)
+ * renormalized (by P_u again if no mass is left). Without an accepted child the bonus is
+ * the lowest token whose cumulative P exceeds bonus_uniforms[u] times the total.
+ * parents, tokens int32 [T]; draft_logits / target_logits fp32 [T][V] (row u: the logits
+ * at node u); uniforms, bonus_uniforms fp64 [T] in [0, 1) (the random numbers, inputs);
+ * outputs as ss_tree_accept (path_out[0 .. L) the accepted nodes, then -1). A token id
+ * outside [0, V) is never accepted. T <= 256; workspace: ss_tree_accept_stochastic_workspace. */
+size_t ss_tree_accept_stochastic_workspace(int32_t T, int32_t V);
+ss_status ss_tree_accept_stochastic(const int32_t* parents, const int32_t* tokens, const float* draft_logits,
+                                    const float* target_logits, int32_t T, int32_t V, float inv_t_draft,
+                                    float inv_t_target, const double* uniforms, const double* bonus_uniforms,
+                                    int32_t* path_out, int32_t* accept_len_out, int32_t* bonus_out, void* workspace,
+                                    size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------------
  * Draft-tree expansion ([Review] §6.3-§6.4: a static tree, k = 6 children per expanded
  * node, depth 48 (§3.7); [Summary] "Approach": draft probabilities sharpened at

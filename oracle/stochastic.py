@@ -9,7 +9,9 @@ do not spell the tree rule out; this is the plain multi-round form of the same t
 
 * P_u = softmax(y_t) with y_t = fp32(target_logits[u] * fp32(1 / t_target)), and
   Q_u = softmax(y_d) with y_d = fp32(draft_logits[u] * fp32(1 / t_draft)): the target's
-  and the draft's distributions at node u; probabilities in fp64.
+  and the draft's distributions at node u. Precision (the decisions below are taken in
+  it on both sides): e(v) = fp32 exp of fp32(y(v) - max y), widened to fp64; the
+  normalizer and every later quantity in fp64.
 * From the root, at node u the children c (in index order) are tried: child c with
   token x is accepted iff uniforms[c] * Q_u(x) < P(x) (u < P / Q; strict, so a token the
   target cannot emit is never accepted), P the current residual (P_u at first); then the
@@ -28,8 +30,8 @@ import numpy as np
 
 def probs(logits_row, inv_temp):
     y = np.asarray(logits_row, dtype=np.float32) * np.float32(inv_temp)
-    y64 = y.astype(np.float64)
-    e = np.exp(y64 - y64.max())
+    d = (y - y.max()).astype(np.float32)
+    e = np.exp(d).astype(np.float64)
     return e / e.sum()
 
 
