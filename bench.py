@@ -637,6 +637,25 @@ def main():
     e0.record(); g_verify.replay(); e1.record(); torch.cuda.synchronize()
     ms_verify = e0.elapsed_time(e1)
     step_bytes = algorithmic_bytes_step(cfg, n_layers, logit_rows=R)
+
+    # stochastic verification at target temperature 0.6 on the cycle's finished tree (outside
+    # the timed cycle): the verify pass's target logits, the draft's logits of every node
+    # from one extra all-rows draft step, seeded uniforms
+    d_all = torch.empty((T, V), dtype=torch.float32, device=dev)
+    draft.draft_tree_step(parents, C, tk_d, tv_d, tokens=tokens, logits=d_all, workspace=ws_d)
+    rng_u = np.random.default_rng(7)
+    uni = torch.from_numpy(rng_u.random(T)).to(dev)
+    buni = torch.from_numpy(rng_u.random(T)).to(dev)
+    inv_tt = float(np.float32(1.0) / np.float32(0.6))
+    sv_out = bq.tree_accept_stochastic(parents, tokens, d_all, vlogits, inv_t, inv_tt, uni, buni)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(5):
+        bq.tree_accept_stochastic(parents, tokens, d_all, vlogits, inv_t, inv_tt, uni, buni, out=sv_out)
+    e1.record(); torch.cuda.synchronize()
+    ms_stochastic = e0.elapsed_time(e1) / 5
+    sv_len = int(sv_out[1].item())
+    del d_all
     step_gbs = step_bytes / (ms_draft_step * 1e-3) / 1e9
 
     # dominant kernel: fused int4 gate_up + SwiGLU, 8 layers' weights in rotation (> 256 MB
@@ -710,6 +729,7 @@ def main():
                    "draft_step_ms": round(ms_draft_step, 4), "verify_ms": round(ms_verify, 4),
                    "draft_step_alg_bytes": int(step_bytes),
                    "draft_step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                   "stochastic_verify_ms": round(ms_stochastic, 4), "stochastic_accept_len": sv_len,
                    "other_workloads": extra},
         "roofline": {"kernel": "w4k_kernel<TT=4, EPI_SWIGLU, tiled> (tiled int4 gate_up 37888x3584, T=64)",
                      "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
