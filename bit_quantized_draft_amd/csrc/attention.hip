@@ -64,8 +64,8 @@ hipError_t launch_tree_mask(const int32_t* parents, int T, uint64_t* mask, int32
 
 // ------------------------------------------------------------------ attention
 
-// One query tile per row wave (short contexts): NKQ1 key groups of NSUB1 sub-tiles each.
-// Several query tiles per row wave (long contexts): one key group of NSUB sub-tiles.
+// One query tile per row wave: NKQ1 key groups of NSUB1 sub-tiles each. Two query tiles
+// per row wave (many query rows over long contexts): NKQ key groups of NSUB sub-tiles.
 #ifndef SS_ATTN_NSUB
 #define SS_ATTN_NSUB 2
 #endif
@@ -75,10 +75,14 @@ hipError_t launch_tree_mask(const int32_t* parents, int T, uint64_t* mask, int32
 #ifndef SS_ATTN_NKQ1
 #define SS_ATTN_NKQ1 4
 #endif
+#ifndef SS_ATTN_NKQ
+#define SS_ATTN_NKQ 2
+#endif
 constexpr int ATT_NSUB = SS_ATTN_NSUB;
 constexpr int ATT_NSUB1 = SS_ATTN_NSUB1;
 constexpr int ATT_NKQ1 = SS_ATTN_NKQ1;
-static int attn_kt(int qc) { return qc == 1 ? 32 * ATT_NSUB1 * ATT_NKQ1 : 32 * ATT_NSUB; }
+constexpr int ATT_NKQ = SS_ATTN_NKQ;
+static int attn_kt(int qc) { return qc == 1 ? 32 * ATT_NSUB1 * ATT_NKQ1 : 32 * ATT_NSUB * ATT_NKQ; }
 
 struct AttnParams {
   const uint16_t* q;
@@ -440,11 +444,12 @@ __global__ __launch_bounds__(HD) void attn_merge_kernel(AttnParams p, uint16_t* 
   if (out_f32) out_f32[o] = v;
 }
 
-// 16-row query tiles per wave. Measured on MI355X: one tile per wave (more workgroups,
-// fewer registers) is fastest up to ~4K keys; long contexts favour three while one
-// workgroup then covers all query rows of a KV head (fewer workgroups re-reading each
-// K/V tile), and two once the rows need several workgroups anyway (1280 rows over 4352
-// keys: 142 us against 163 us with three).
+// 16-row query tiles per wave. Measured on MI355X (attention kernel alone): one tile per
+// wave, four key groups, is fastest up to 4K keys and for up to 192 query rows per KV head
+// at any length (192 rows over 16432 keys: 48 us, against 62 us with three tiles per wave
+// and one workgroup per KV head); many rows over long contexts take two tiles per wave and
+// two key groups (1280 rows over 4352 keys: 78 us, against 112 us with one key group and
+// 108 us with one tile).
 // Tuning overrides (build-time): SS_ATTN_QC forces the query tiles per wave (0 = the rule
 // below); SS_ATTN_WGS is the workgroup count the key split aims for. Measured at the
 // Qwen2.5-7B / Llama-3.1-8B shapes, 128 and 512 workgroups are no faster than 256.
@@ -456,8 +461,7 @@ __global__ __launch_bounds__(HD) void attn_merge_kernel(AttnParams p, uint16_t* 
 #endif
 static int attn_qc(int rows, int keys) {
   if (SS_ATTN_QC > 0) return SS_ATTN_QC;
-  const int qc = (rows <= 64) ? 1 : (rows <= 128) ? 2 : (rows <= 192) ? 3 : 2;
-  return keys <= 4096 ? 1 : qc;
+  return (keys <= 4096 || rows <= 192) ? 1 : 2;
 }
 
 AttnPlan plan_attention(int T, int C, int nq, int nkv, int hd) {
@@ -496,15 +500,13 @@ hipError_t launch_attention(const AttnArgs& a, const AttnPlan& pl, void* ws, hip
   const int qc = attn_qc(p.rows, a.C + a.T);
   dim3 grid(pl.qblocks, a.nkv, pl.splits);
   if (pl.keys_per_split % attn_kt(qc)) return hipErrorInvalidValue;   // a plan for another shape
-  const dim3 blk1(256 * ATT_NKQ1), blk(256);
+  const dim3 blk1(256 * ATT_NKQ1), blk(256 * ATT_NKQ);
   if (a.hd == 128) {
     if (qc == 1) hipLaunchKernelGGL((tree_attn_kernel<128, 1, ATT_NSUB1, ATT_NKQ1>), grid, blk1, 0, st, p);
-    else if (qc == 2) hipLaunchKernelGGL((tree_attn_kernel<128, 2, ATT_NSUB, 1>), grid, blk, 0, st, p);
-    else hipLaunchKernelGGL((tree_attn_kernel<128, 3, ATT_NSUB, 1>), grid, blk, 0, st, p);
+    else hipLaunchKernelGGL((tree_attn_kernel<128, 2, ATT_NSUB, ATT_NKQ>), grid, blk, 0, st, p);
   } else {
     if (qc == 1) hipLaunchKernelGGL((tree_attn_kernel<64, 1, ATT_NSUB1, ATT_NKQ1>), grid, blk1, 0, st, p);
-    else if (qc == 2) hipLaunchKernelGGL((tree_attn_kernel<64, 2, ATT_NSUB, 1>), grid, blk, 0, st, p);
-    else hipLaunchKernelGGL((tree_attn_kernel<64, 3, ATT_NSUB, 1>), grid, blk, 0, st, p);
+    else hipLaunchKernelGGL((tree_attn_kernel<64, 2, ATT_NSUB, ATT_NKQ>), grid, blk, 0, st, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
