@@ -64,6 +64,13 @@ hipError_t launch_tree_mask(const int32_t* parents, int T, uint64_t* mask, int32
 
 // ------------------------------------------------------------------ attention
 
+// Two floats to packed bf16, round to nearest even (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pk_bf16_rne(float a, float b) {
+  typedef float f2v __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2v __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2v){a, b}, b2v));
+}
+
 // One query tile per row wave: NKQ1 key groups of NSUB1 sub-tiles each. Two query tiles
 // per row wave (many query rows over long contexts): NKQ key groups of NSUB sub-tiles.
 #ifndef SS_ATTN_NSUB
@@ -188,7 +195,37 @@ __global__ __launch_bounds__(256 * NKQ) void tree_attn_kernel(AttnParams p) {
     dc = (l >> 3) + 8 * (w / KPW);
     return u < VU;   // whole waves
   };
+  // per-thread element offsets of the tile's K / V chunks (loop-invariant)
+  int koff[KCH], voff[VCH];
+#pragma unroll
+  for (int i = 0; i < KCH; ++i) {
+    const int ci = tid + i * NW * 64;
+    koff[i] = (ci / (HD / 8)) * HD + (ci % (HD / 8)) * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < VCH; ++i) {
+    int kp, dc;
+    v_unit(i, kp, dc);
+    voff[i] = 2 * kp * HD + dc * 8;
+  }
   auto load_tile = [&](int k0) {
+    if (k0 + KT <= min(p.C, key_end)) {
+      // the whole tile lies in the prefix cache and in the split: one uniform base
+      const size_t row0 = ((size_t)kv * p.c_stride + k0) * HD;
+      const uint16_t* kb = p.kc + row0;
+      const uint16_t* vb = p.vc + row0;
+#pragma unroll
+      for (int i = 0; i < KCH; ++i) kreg[i] = *reinterpret_cast<const u32x4_t*>(kb + koff[i]);
+#pragma unroll
+      for (int i = 0; i < VCH; ++i) {
+        int kp, dc;
+        if (v_unit(i, kp, dc)) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) vreg[i][h] = *reinterpret_cast<const u32x4_t*>(vb + voff[i] + h * HD);
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int ci = tid + i * NW * 64;
@@ -274,9 +311,8 @@ __global__ __launch_bounds__(256 * NKQ) void tree_attn_kernel(AttnParams p) {
         for (int kt = 0; kt < 2 * NSUB; ++kt)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float v = s[c][kt][e] * p.scale_log2;
-            s[c][kt][e] = v;
-            mx = fmaxf(mx, v);
+            s[c][kt][e] *= p.scale_log2;
+            mx = fmaxf(mx, s[c][kt][e]);
           }
       } else {
 #pragma unroll
@@ -300,7 +336,9 @@ __global__ __launch_bounds__(256 * NKQ) void tree_attn_kernel(AttnParams p) {
       const bool move = mx > m_run[c] + 8.0f;   // always true on a row's first finite tile
       const float m_new = move ? fmaxf(m_run[c], mx) : m_run[c];
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2f(m_run[c] - m_use);   // exp2(-inf) = 0 on the first tile
+      // v_exp_f32 straight (no denormal range scaling): arguments are <= 8 or -inf, and
+      // results below 2^-126, which it may flush to zero, are far below the row sum (>= 1)
+      const float alpha = __builtin_amdgcn_exp2f(m_run[c] - m_use);   // 0 on the first tile
       const bool any_move = __builtin_amdgcn_ballot_w64(move) != 0;
       float psum = 0.f;
       uint32_t pk[NSUB][4];
@@ -311,11 +349,11 @@ __global__ __launch_bounds__(256 * NKQ) void tree_attn_kernel(AttnParams p) {
           float pv[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            pv[e] = exp2f(s[c][2 * sub + h][e] - m_use);
+            pv[e] = __builtin_amdgcn_exp2f(s[c][2 * sub + h][e] - m_use);
             psum += pv[e];
           }
-          pk[sub][h * 2 + 0] = pack_bf16x2(pv[0], pv[1]);
-          pk[sub][h * 2 + 1] = pack_bf16x2(pv[2], pv[3]);
+          pk[sub][h * 2 + 0] = pk_bf16_rne(pv[0], pv[1]);
+          pk[sub][h * 2 + 1] = pk_bf16_rne(pv[2], pv[3]);
         }
       psum += __shfl_xor(psum, 16, 64);
       psum += __shfl_xor(psum, 32, 64);
