@@ -47,6 +47,10 @@ def parse():
     ap.add_argument("--pmc-probe", action="store_true",
                     help="run only the dominant kernel over rotated weights, then a 256 MiB "
                          "negation as the counter calibration (for rocprofv3 --pmc passes)")
+    ap.add_argument("--attn-probe", action="store_true",
+                    help="run only the tree attention (attention kernel + split merge) at the "
+                         "Qwen2.5-7B (T=64, C=2048) and Llama-3.1-8B (T=48, C=16384) shapes over "
+                         "rotated KV caches, then the 256 MiB negation (for rocprofv3 passes)")
     ap.add_argument("--mfma-probe", action="store_true",
                     help="MFMA utilisation at the large-tree workload: the four tiled int4 linears "
                          "of a Qwen2.5-32B-shaped layer at T=256, timed against the dense bf16 peak")
@@ -340,6 +344,41 @@ def pmc_probe(args):
           flush=True)
 
 
+def attn_probe(args):
+    """Tree attention alone at two shapes, each over enough KV-cache copies in rotation to
+    exceed the 256 MB Infinity Cache (as in the draft step, where a layer's cache was last
+    read a whole step earlier): Qwen2.5-7B (28 query / 4 KV heads, T=64 CB tree, C=2048,
+    64 copies of 4.3 MB) and Llama-3.1-8B (32 / 8 heads, T=48 CB tree, C=16384, 5 copies of
+    67 MB). kernel_reps launches of each, then the calibration negation."""
+    import torch
+    import bit_quantized_draft_amd as bq
+    from synth import gen
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    for name, T, C, nq, nkv, copies, cid in (("qwen2.5-7b", 64, 2048, 28, 4, 64, 3),
+                                            ("llama3.1-8b", 48, 16384, 32, 8, 5, 5)):
+        hd = 128
+        rnd = lambda shape, tid, layer: gen.torch_normal_bf16(shape, 1.0, 0, cid, tid, layer, dev)
+        q = rnd((T, nq, hd), gen.TID_Q, 0)
+        kv = [(rnd((nkv, C, hd), gen.TID_KC, i), rnd((nkv, C, hd), gen.TID_VC, i)) for i in range(copies)]
+        kt = rnd((nkv, T, hd), gen.TID_KT, 0)
+        vt = rnd((nkv, T, hd), gen.TID_VT, 0)
+        par = torch.from_numpy(gen.tree_parents(T, "CB", seed=0, cid=cid)).to(dev)
+        torch.cuda.synchronize()
+        for r in range(args.kernel_reps):
+            for kc, vc in kv:
+                bq.tree_attention(q, kc, vc, kt, vt, par, C)
+        torch.cuda.synchronize()
+        print(f"attn probe {name}: {args.kernel_reps * copies} launches", flush=True)
+        del kv
+    a = torch.ones(CAL_BYTES // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    print(f"attn probe done: one {CAL_BYTES >> 20} MiB negation", flush=True)
+
+
 MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 
 
@@ -498,6 +537,9 @@ def main():
         return
     if args.mfma_probe:
         mfma_probe(args)
+        return
+    if args.attn_probe:
+        attn_probe(args)
         return
     if args.extra_only:
         import torch

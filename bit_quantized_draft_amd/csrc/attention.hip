@@ -71,25 +71,13 @@ __device__ __forceinline__ uint32_t pk_bf16_rne(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2v){a, b}, b2v));
 }
 
-// One query tile per row wave: NKQ1 key groups of NSUB1 sub-tiles each. Two query tiles
-// per row wave (many query rows over long contexts): NKQ key groups of NSUB sub-tiles.
-#ifndef SS_ATTN_NSUB
-#define SS_ATTN_NSUB 2
-#endif
-#ifndef SS_ATTN_NSUB1
-#define SS_ATTN_NSUB1 1
-#endif
-#ifndef SS_ATTN_NKQ1
-#define SS_ATTN_NKQ1 4
-#endif
-#ifndef SS_ATTN_NKQ
-#define SS_ATTN_NKQ 2
-#endif
-constexpr int ATT_NSUB = SS_ATTN_NSUB;
-constexpr int ATT_NSUB1 = SS_ATTN_NSUB1;
-constexpr int ATT_NKQ1 = SS_ATTN_NKQ1;
-constexpr int ATT_NKQ = SS_ATTN_NKQ;
-static int attn_kt(int qc) { return qc == 1 ? 32 * ATT_NSUB1 * ATT_NKQ1 : 32 * ATT_NSUB * ATT_NKQ; }
+// Three workgroup shapes, all with 128-key tiles: (query tiles per row wave, 32-key
+// sub-tiles per key group, key groups) = (1, 2, 2) for contexts up to 4K keys, (1, 1, 4)
+// for up to 192 query rows per KV head over longer contexts, (2, 2, 2) otherwise.
+constexpr int ATT_KT = 128;
+struct AttnShape {
+  int qc, nsub, nkq;
+};
 
 struct AttnParams {
   const uint16_t* q;
@@ -482,33 +470,30 @@ __global__ __launch_bounds__(HD) void attn_merge_kernel(AttnParams p, uint16_t* 
   if (out_f32) out_f32[o] = v;
 }
 
-// 16-row query tiles per wave. Measured on MI355X (attention kernel alone): one tile per
-// wave, four key groups, is fastest up to 4K keys and for up to 192 query rows per KV head
-// at any length (192 rows over 16432 keys: 48 us, against 62 us with three tiles per wave
-// and one workgroup per KV head); many rows over long contexts take two tiles per wave and
-// two key groups (1280 rows over 4352 keys: 78 us, against 112 us with one key group and
-// 108 us with one tile).
-// Tuning overrides (build-time): SS_ATTN_QC forces the query tiles per wave (0 = the rule
-// below); SS_ATTN_WGS is the workgroup count the key split aims for. Measured at the
-// Qwen2.5-7B / Llama-3.1-8B shapes, 128 and 512 workgroups are no faster than 256.
-#ifndef SS_ATTN_QC
-#define SS_ATTN_QC 0
-#endif
+// Measured on MI355X (attention kernel alone): up to 4K keys, (1, 2, 2) beats (1, 1, 4) by
+// about 1 us (288 rows over 1072 keys: 12.1 us against 13.1 us; 448 rows over 2112 keys:
+// 14.1 against 15.1). Longer contexts with up to 192 rows per KV head: (1, 1, 4), 44 us for
+// 192 rows over 16432 keys, against 49 us with (1, 2, 2) and 62 us with three tiles per wave
+// and one workgroup per KV head. Many rows over long contexts: (2, 2, 2), 65 us for 1280
+// rows over 4352 keys, against 112 us with one key group and 108 us with one tile per wave.
+// SS_ATTN_WGS (build-time) is the workgroup count the key split aims for; at the
+// Qwen2.5-7B / Llama-3.1-8B shapes 128 and 512 are no faster than 256.
 #ifndef SS_ATTN_WGS
 #define SS_ATTN_WGS 256
 #endif
-static int attn_qc(int rows, int keys) {
-  if (SS_ATTN_QC > 0) return SS_ATTN_QC;
-  return (keys <= 4096 || rows <= 192) ? 1 : 2;
+static AttnShape attn_shape(int rows, int keys) {
+  if (keys <= 4096) return {1, 2, 2};
+  if (rows <= 192) return {1, 1, 4};
+  return {2, 2, 2};
 }
 
 AttnPlan plan_attention(int T, int C, int nq, int nkv, int hd) {
   AttnPlan pl;
   const int grp = nq / nkv;
   const int rows = grp * T;
-  // query-row blocks of 4 row waves x QC x 16 rows; QC picked at launch from rows
-  const int qc = attn_qc(rows, C + T);
-  const int KT = attn_kt(qc);
+  // query-row blocks of 4 row waves x QC x 16 rows
+  const int qc = attn_shape(rows, C + T).qc;
+  const int KT = ATT_KT;
   pl.qblocks = (rows + 4 * qc * 16 - 1) / (4 * qc * 16);
   const int keys = C + T;
   const int units = pl.qblocks * nkv;
@@ -535,17 +520,19 @@ hipError_t launch_attention(const AttnArgs& a, const AttnPlan& pl, void* ws, hip
   p.scale_log2 = a.sm_scale * 1.4426950408889634f;
   p.o_part = reinterpret_cast<float*>(ws);
   p.ml_part = p.o_part + (size_t)pl.splits * a.nkv * p.rows * a.hd;
-  const int qc = attn_qc(p.rows, a.C + a.T);
+  const AttnShape sh = attn_shape(p.rows, a.C + a.T);
   dim3 grid(pl.qblocks, a.nkv, pl.splits);
-  if (pl.keys_per_split % attn_kt(qc)) return hipErrorInvalidValue;   // a plan for another shape
-  const dim3 blk1(256 * ATT_NKQ1), blk(256 * ATT_NKQ);
-  if (a.hd == 128) {
-    if (qc == 1) hipLaunchKernelGGL((tree_attn_kernel<128, 1, ATT_NSUB1, ATT_NKQ1>), grid, blk1, 0, st, p);
-    else hipLaunchKernelGGL((tree_attn_kernel<128, 2, ATT_NSUB, ATT_NKQ>), grid, blk, 0, st, p);
-  } else {
-    if (qc == 1) hipLaunchKernelGGL((tree_attn_kernel<64, 1, ATT_NSUB1, ATT_NKQ1>), grid, blk1, 0, st, p);
-    else hipLaunchKernelGGL((tree_attn_kernel<64, 2, ATT_NSUB, ATT_NKQ>), grid, blk, 0, st, p);
-  }
+  if (pl.keys_per_split % ATT_KT) return hipErrorInvalidValue;   // a plan for another shape
+  const dim3 blk(256 * sh.nkq);
+#define ATT_LAUNCH(HD)                                                                                     \
+  do {                                                                                                    \
+    if (sh.qc == 2) hipLaunchKernelGGL((tree_attn_kernel<HD, 2, 2, 2>), grid, blk, 0, st, p);             \
+    else if (sh.nkq == 4) hipLaunchKernelGGL((tree_attn_kernel<HD, 1, 1, 4>), grid, blk, 0, st, p);      \
+    else hipLaunchKernelGGL((tree_attn_kernel<HD, 1, 2, 2>), grid, blk, 0, st, p);                        \
+  } while (0)
+  if (a.hd == 128) ATT_LAUNCH(128);
+  else ATT_LAUNCH(64);
+#undef ATT_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.hd == 128)
