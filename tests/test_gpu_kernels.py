@@ -151,6 +151,10 @@ def _attn_case(T, C, nq, nkv, hd, kind, seed, c_stride=None):
     (37, 77, 8, 2, 128, "RB"),         # ragged key tiles
     (256, 300, 40, 8, 128, "RB"),      # 32B-shaped head groups, 256-node tree
     (48, 16384, 32, 8, 128, "CB"),     # long context (Llama-8B-shaped)
+    # one workgroup shape each past 4K keys: up to 192 query rows per KV head, and more
+    (40, 4500, 8, 2, 64, "CB"),        # 160 rows, hd 64
+    (64, 4200, 16, 4, 64, "RB"),       # 256 rows, hd 64
+    (64, 4200, 16, 4, 128, "CB"),      # 256 rows, hd 128
 ])
 def test_tree_attention_parity(T, C, nq, nkv, hd, kind):
     print(f"attention T={T} C={C} nq={nq} nkv={nkv} hd={hd}", flush=True)
