@@ -189,3 +189,52 @@ def test_no_device_is_reported_not_crashed(L):
     assert L.ss_w4a16_linear_tiled_noalloc(ok, 4, ok, 16, 128, ok, None, None) == _lib.SS_ERR_DEVICE
     assert L.ss_row_argmax(ctypes.cast(ok, ctypes.POINTER(ctypes.c_float)), 4, 100,
                            ctypes.cast(ok, ctypes.POINTER(ctypes.c_int32)), None) == _lib.SS_ERR_DEVICE
+
+
+# ------------------------------------------------------------------ sanitizers
+
+def _sources_objects(tmp):
+    """Objects of every source but the C ABI itself: the in-tree build's where they are at
+    least as new as their sources, else compiled afresh into `tmp`."""
+    from bit_quantized_draft_amd import build
+    objs = []
+    for src in build.SOURCES:
+        if src == "api.cpp":
+            continue
+        o = os.path.join(build.BUILD, os.path.splitext(src)[0] + ".o")
+        if not os.path.exists(o) or os.path.getmtime(o) < os.path.getmtime(os.path.join(build.CSRC, src)):
+            o = build._compile(src, str(tmp))
+        objs.append(o)
+    return objs
+
+
+def test_host_checks_under_sanitizers(tmp_path):
+    """The host half of the C ABI (argument checks, messages, the no-device path) built
+    with AddressSanitizer and UndefinedBehaviorSanitizer, driven by a C program that makes
+    invalid calls; no call reaches a GPU. The device code is built as usual."""
+    import shutil
+    import subprocess
+    from bit_quantized_draft_amd import build
+    clang = "/opt/rocm/llvm/bin/clang"
+    if not (os.path.exists(build.HIPCC) and os.path.exists(clang)):
+        pytest.skip("hipcc / clang not available")
+    objs = _sources_objects(tmp_path)
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined"]
+    api_o, drv_o, exe = str(tmp_path / "api_san.o"), str(tmp_path / "driver.o"), str(tmp_path / "driver")
+    steps = [
+        [build.HIPCC, "-x", "hip", "--cuda-host-only", "-O1", "-g", "-std=c++17", "-fPIC", *san,
+         "-fno-omit-frame-pointer", "-c", os.path.join(build.CSRC, "api.cpp"), "-o", api_o],
+        [clang, "-O1", "-g", "-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-Wall", "-c",
+         os.path.join(ROOT, "tests", "host_sanitize", "driver.c"), "-o", drv_o],
+        [build.HIPCC, "--offload-arch=gfx950", *san, drv_o, api_o, *objs, "-o", exe],
+    ]
+    for cmd in steps:
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        assert r.returncode == 0, r.stdout + r.stderr
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0", UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1",
+               HIP_VISIBLE_DEVICES="-1")
+    r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=120)
+    out = r.stdout + r.stderr
+    assert "AddressSanitizer" not in out and "runtime error" not in out, out
+    assert r.returncode == 0 and "PASSED" in r.stdout, out
+    shutil.rmtree(tmp_path, ignore_errors=True)
