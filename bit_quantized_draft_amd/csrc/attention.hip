@@ -470,6 +470,47 @@ __global__ __launch_bounds__(HD) void attn_merge_kernel(AttnParams p, uint16_t* 
   if (out_f32) out_f32[o] = v;
 }
 
+// The same merge with a workgroup of 256 threads over MR query rows, a thread taking 4
+// consecutive d of one row; faster when there are many rows (10240 (row, KV head) pairs:
+// 6.1 us against 9.4 us), slower with few (1792 pairs: 6.4 against 5.1 us).
+constexpr int MERGE_WIDE_THREADS = 256;
+template <int HD>
+__global__ __launch_bounds__(MERGE_WIDE_THREADS) void attn_merge_wide_kernel(AttnParams p, uint16_t* out,
+                                                                           float* out_f32) {
+  constexpr int TPR = HD / 4;                        // threads per row
+  constexpr int MR = MERGE_WIDE_THREADS / TPR;       // rows per workgroup
+  const int kv = blockIdx.y;
+  const int r = blockIdx.x * MR + threadIdx.x / TPR;
+  const int d = (threadIdx.x % TPR) * 4;
+  if (r >= p.rows) return;
+  const size_t stride = (size_t)p.nkv * p.rows;      // between splits, in rows
+  const size_t row0 = (size_t)kv * p.rows + r;
+  float M = -INFINITY;
+#pragma unroll 8
+  for (int s = 0; s < p.splits; ++s) M = fmaxf(M, p.ml_part[(row0 + s * stride) * 2]);
+  const float Mu = (M == -INFINITY) ? 0.f : M;
+  float L = 0.f;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+  for (int s = 0; s < p.splits; ++s) {
+    const size_t base = row0 + s * stride;
+    const float w = exp2f(p.ml_part[base * 2] - Mu);
+    L += w * p.ml_part[base * 2 + 1];
+    const f32x4_t o4 = *reinterpret_cast<const f32x4_t*>(p.o_part + base * HD + d);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += w * o4[e];
+  }
+  const int t = r / p.grp, h = kv * p.grp + r % p.grp;
+  const size_t o = ((size_t)t * p.nq + h) * HD + d;
+  // element stores: the outputs need only their element alignment
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float v = acc[e] / L;
+    if (out) out[o + e] = f32_to_bf16(v);
+    if (out_f32) out_f32[o + e] = v;
+  }
+}
+
 // Measured on MI355X (attention kernel alone): up to 4K keys, (1, 2, 2) beats (1, 1, 4) by
 // about 1 us (288 rows over 1072 keys: 12.1 us against 13.1 us; 448 rows over 2112 keys:
 // 14.1 against 15.1). Longer contexts with up to 192 rows per KV head: (1, 1, 4), 44 us for
@@ -535,10 +576,18 @@ hipError_t launch_attention(const AttnArgs& a, const AttnPlan& pl, void* ws, hip
 #undef ATT_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.hd == 128)
+  if ((long long)p.rows * a.nkv >= 4096) {
+    if (a.hd == 128)
+      hipLaunchKernelGGL((attn_merge_wide_kernel<128>), dim3((p.rows + 7) / 8, a.nkv), dim3(MERGE_WIDE_THREADS), 0,
+                         st, p, a.out, a.out_f32);
+    else
+      hipLaunchKernelGGL((attn_merge_wide_kernel<64>), dim3((p.rows + 15) / 16, a.nkv), dim3(MERGE_WIDE_THREADS), 0,
+                         st, p, a.out, a.out_f32);
+  } else if (a.hd == 128) {
     hipLaunchKernelGGL((attn_merge_kernel<128>), dim3(p.rows, a.nkv), dim3(128), 0, st, p, a.out, a.out_f32);
-  else
+  } else {
     hipLaunchKernelGGL((attn_merge_kernel<64>), dim3(p.rows, a.nkv), dim3(64), 0, st, p, a.out, a.out_f32);
+  }
   return hipGetLastError();
 }
 

@@ -155,6 +155,7 @@ def _attn_case(T, C, nq, nkv, hd, kind, seed, c_stride=None):
     (40, 4500, 8, 2, 64, "CB"),        # 160 rows, hd 64
     (64, 4200, 16, 4, 64, "RB"),       # 256 rows, hd 64
     (64, 4200, 16, 4, 128, "CB"),      # 256 rows, hd 128
+    (256, 200, 16, 4, 64, "RB"),       # 4096 (row, KV head) pairs: the wide merge, hd 64
 ])
 def test_tree_attention_parity(T, C, nq, nkv, hd, kind):
     print(f"attention T={T} C={C} nq={nq} nkv={nkv} hd={hd}", flush=True)
