@@ -193,6 +193,43 @@ def test_step_error_word_under_debug_sync():
     assert res["bad_logit_row"].startswith("SS_ERR_INVALID_ARG") and "logit row" in res["bad_logit_row"]
 
 
+def test_28_layer_stack_drift():
+    """Drift over the depth of a 7B-sized stack: 28 substitute layers (a narrower width,
+    H=512, I=1536, so that the fp64 oracle stays quick) with the LM head, T=64 CB tree,
+    C=256. Reported (DRIFT line) and held to a bound twice the single-layer one; the
+    per-layer parity tests above carry the real gate."""
+    L, T, C, V = 28, 64, 256, 4096
+    cfg = small_cfg(cid=10, H=512, I=1536, nq=8, nkv=2, hd=64)
+    print(f"stack drift L={L} T={T} C={C} H={cfg.H}", flush=True)
+    layers = [make_layer(cfg, li, C, seed=4, kind="tiled") for li in range(L)]
+    embed = gen.normal_bf16((V, cfg.H), 1.0, 4, cfg.cid, gen.TID_EMBED)
+    head = gen.normal_bf16((V, cfg.H), 0.05, 4, cfg.cid, gen.TID_LMHEAD)
+    fnorm = gen.norm_gain_bf16(cfg.H, seed=4, cid=cfg.cid, layer=99, random=True)
+    par = gen.tree_parents(T, "CB", seed=4)
+    tok = gen.tree_tokens(par, V, seed=4)
+    model = bq.SubstituteModel(cfg.H, cfg.I, cfg.nq, cfg.nkv, cfg.hd, [d for _, d, _, _ in layers],
+                               V=V, embed=to_bf16(embed), final_norm=to_bf16(fnorm),
+                               lm_head=to_bf16(head), rope_theta=cfg.rope_theta, rms_eps=cfg.eps)
+    dev = torch.device("cuda:0")
+    tk = [torch.empty((cfg.nkv, T, cfg.hd), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    tv = [torch.empty((cfg.nkv, T, cfg.hd), dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    logits = torch.empty((T, V), dtype=torch.float32, device=dev)
+    hout = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev)
+    model.draft_tree_step(to_dev(par), C, tk, tv, tokens=to_dev(tok), hidden_out=hout, logits=logits)
+    torch.cuda.synchronize()
+    ref_h, ref_lg = oracle.stack64(tok, par, C, embed, [o for o, _, _, _ in layers],
+                                   [kc for _, _, kc, _ in layers], [vc for _, _, _, vc in layers],
+                                   fnorm, head, cfg)
+    got_h = oracle.bf16_to_f64(bf16_bits(hout))
+    got_lg = host(logits).astype(np.float64)
+    rel = lambda g, r: float(np.linalg.norm(g - r) / np.linalg.norm(r))
+    agree = float(np.mean(np.argmax(got_lg, axis=1) == np.argmax(ref_lg, axis=1)))
+    print(f"DRIFT 28 layers: hidden rel-L2 {rel(got_h, ref_h):.3e}, logits rel-L2 {rel(got_lg, ref_lg):.3e}, "
+          f"top-1 agreement {agree:.3f}", flush=True)
+    assert_close(got_h, ref_h, rel_l2=2e-2, max_abs=4e-2, scale_abs=True, bf16_out=True, what="28-layer hidden")
+    assert_close(got_lg, ref_lg, rel_l2=2e-2, max_abs=4e-2, scale_abs=True, what="28-layer logits")
+
+
 def test_tiled_step_is_bit_identical_to_plain():
     """The tiled weights change where the codes live, not the arithmetic: the whole
     step's outputs match the plain layout's bit for bit (7B-shaped layer, T = 64)."""
