@@ -252,43 +252,77 @@ def extra_config(cid, args, dev):
 
 # ------------------------------------------------------------------ CPU oracle baseline
 
-def cpu_baseline(cfg, n_layers):
+def cpu_baseline(cfg, n_layers, R):
+    """The oracle timed on the host, as a whole decode cycle like the GPU's `value`: 48
+    draft steps (n_layers substitute layers + the LM head on R frontier rows) and one
+    verify pass (n_layers bf16 target layers + the LM head on all T rows). Each layer kind
+    is timed once per repeat (3 repeats: mean and std); the LM head on 1/16 of its rows,
+    scaled. Also one 7B-shaped substitute layer at T=48, C=1024 (the one-layer workload)
+    and the 512-wide linear + attention case (T=16, C=128) on one thread."""
     import oracle
     from synth import gen
-    from synth.configs import layer_shapes
+    from synth.configs import get_config, layer_shapes
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([i.get("num_threads", 1) for i in threadpool_info()
                        if i.get("user_api") == "blas"] or [1])
     except Exception:
+        threadpool_limits = None
         threads = os.cpu_count() or 1
     T, C = cfg.T, cfg.C
     log("cpu baseline: generating and quantizing one layer with the oracle (untimed)")
-    lw = {}
+    sub, tgt = {}, {}
     for name, N, K in layer_shapes(cfg):
         w = gen.weight_bf16(N, K, cfg.w_std, seed=0, cid=cfg.cid, layer=0, slot=gen.SLOT[name])
-        lw[name] = oracle.quantize(w)
-    lw["norm1"] = gen.norm_gain_bf16(cfg.H)
-    lw["norm2"] = gen.norm_gain_bf16(cfg.H)
+        sub[name] = oracle.quantize(w)
+        tgt[name] = w
+    for lw in (sub, tgt):
+        lw["norm1"] = gen.norm_gain_bf16(cfg.H)
+        lw["norm2"] = gen.norm_gain_bf16(cfg.H)
     kc = gen.normal_bf16((cfg.nkv, C, cfg.hd), 1.0, 0, cfg.cid, gen.TID_KC, 0)
     vc = gen.normal_bf16((cfg.nkv, C, cfg.hd), 1.0, 0, cfg.cid, gen.TID_VC, 0)
     par = gen.tree_parents(T, cfg.tree, seed=0, cid=cfg.cid)
-    h = gen.normal_bf16((T, cfg.H), 1.0, 0, cfg.cid, gen.TID_HIDDEN)
+    h = oracle.bf16_to_f64(gen.normal_bf16((T, cfg.H), 1.0, 0, cfg.cid, gen.TID_HIDDEN))
     head_rows = cfg.V // 16
-    head = gen.normal_bf16((head_rows, cfg.H), cfg.w_std, 0, cfg.cid, gen.TID_LMHEAD)
-    t0 = time.perf_counter()
-    oracle.layer64(oracle.bf16_to_f64(h), lw, kc, vc, par, C, cfg)
-    t_layer = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    x = oracle.rmsnorm64(oracle.bf16_to_f64(h), np.ones(cfg.H), cfg.eps)
-    oracle.matmul64(x, oracle.bf16_to_f64(head))
-    t_head = (time.perf_counter() - t0) * (cfg.V / head_rows)
-    t_step = n_layers * t_layer + t_head
-    return {"value": T / t_step, "unit": "draft-tree tokens/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": (f"one substitute layer (T={T}, C={C}, fp64, {t_layer:.2f} s) extrapolated "
-                       f"x{n_layers}, plus the LM head on 1/16 of its rows ({t_head:.2f} s after "
-                       f"scaling x16); one draft step, no verify pass")}
+    head = oracle.bf16_to_f64(gen.normal_bf16((head_rows, cfg.H), cfg.w_std, 0, cfg.cid, gen.TID_LMHEAD))
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    values, parts = [], []
+    for _ in range(3):
+        t_sub = timed(lambda: oracle.layer64(h, sub, kc, vc, par, C, cfg))
+        t_tgt = timed(lambda: oracle.layer64(h, tgt, kc, vc, par, C, cfg))
+        x = oracle.rmsnorm64(h, np.ones(cfg.H), cfg.eps)
+        t_head = timed(lambda: oracle.matmul64(x, head)) * (cfg.V / head_rows)   # all T rows
+        cycle = cfg.steps * (n_layers * t_sub + t_head * R / T) + (n_layers * t_tgt + t_head)
+        values.append(cfg.steps * T / cycle)
+        parts.append((t_sub, t_tgt, t_head, cycle))
+    t_sub, t_tgt, t_head, cycle = (float(np.mean([p[i] for p in parts])) for i in range(4))
+    single = {}
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            c2 = get_config(2)
+            par2 = gen.tree_parents(c2.T, c2.tree, seed=0, cid=c2.cid)
+            h2 = h[:c2.T]
+            t2 = timed(lambda: oracle.layer64(h2, sub, kc[:, :c2.C], vc[:, :c2.C], par2, c2.C, cfg))
+            single["qwen2.5-7b-layer (T=48, C=1024)"] = {"tree_tokens_per_s": round(c2.T / t2, 3),
+                                                         "seconds": round(t2, 3)}
+            c1 = get_config(1)
+            w1 = oracle.quantize(gen.weight_bf16(c1.H, c1.H, 0.02, seed=0, cid=c1.cid))
+            x1 = gen.normal_bf16((c1.T, c1.H), 1.0, 0, c1.cid, gen.TID_X)
+            t1 = timed(lambda: oracle.w4a16_matmul64(x1, *w1))
+            single["linear512 (T=16)"] = {"tree_tokens_per_s": round(c1.T / t1, 3), "seconds": round(t1, 5)}
+    return {"value": float(np.mean(values)), "unit": "draft-tree tokens/s", "cores": int(threads),
+            "kind": "oracle", "std": float(np.std(values)), "repeats": len(values),
+            "single_thread": single,
+            "sample": (f"one decode cycle estimated from timed parts, like the GPU value: "
+                       f"{cfg.steps} x ({n_layers} substitute layers at {t_sub:.2f} s + the LM head "
+                       f"on {R} frontier rows) + one verify pass ({n_layers} bf16 target layers at "
+                       f"{t_tgt:.2f} s + the LM head on all {T} rows, {t_head:.2f} s scaled from 1/16 "
+                       f"of its rows); T={T}, C={C}, fp64; {cycle:.0f} s per cycle; mean of 3 repeats")}
 
 
 # ------------------------------------------------------------------ profiling data
@@ -754,7 +788,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, n_layers)
+        cpu = cpu_baseline(cfg, n_layers, state.R)
 
     line = {
         "metric": "draft-tree tokens/s per substitute-stack step; % of MI355X HBM roofline",
